@@ -1,0 +1,281 @@
+"""Benchmark: streamed frames/s of the 24-block paged-attention hot path.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 518x378]
+
+A step is one frame of the stream through the whole hot path: for each of the
+24 blocks, append the frame's K/V to the block's pages, evict, plan (block 0)
+and run the paged attention; non-keyframes are then rolled back.  The first
+W frames are untimed and fill the scale pages and the live window, so the K
+timed frames run at steady state.  Inputs (Q, K, V of every block for a bank
+of frames, synthetic N(0,1) bf16) are resident in HBM before the timed region.
+
+Alongside the throughput it reports the roofline of the attention kernel (its
+algorithmic bf16 flops over its duration measured with HIP events on the
+stream it runs on), the append kernel's bandwidth, and the CPU oracle timed on
+a bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "streamed frames/s (24-block paged attn, 999-token pages); % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=160)
+    ap.add_argument("--workload", default="518x378")
+    ap.add_argument("--bank", type=int, default=16, help="distinct input frames")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=2,
+                    help="blocks of the oracle frame timed (scaled to all)")
+    ap.add_argument("--no-events", action="store_true",
+                    help="time without per-kernel events (roofline omitted)")
+    return ap.parse_args()
+
+
+def frame_schedule(wl, n):
+    import synth
+    dec = synth.accept_decisions(wl, n) if wl.dynamic else None
+    out = []
+    for f in range(n):
+        if wl.dynamic:
+            out.append("accept" if dec[f] else "reject")
+        else:
+            out.append("key" if synth.is_keyframe(wl, f) else "transient")
+    return out
+
+
+def cpu_baseline(wl, warm_frames, n_blocks_timed):
+    """The oracle, as it is, on the host cores: warm its state machine through
+    the stream (untimed, block 0's pool fed seeded bits), then time one
+    steady-state frame: append + evict + plan on every block and the dense
+    float64 attention of n_blocks_timed blocks (each a full 1005-row query
+    over block 0's gathered K/V), scaled to all blocks."""
+    import numpy as np
+    from oracle import OracleConfig, PagePoolOracle
+    from oracle.attention import paged_attention
+
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    o = PagePoolOracle(cfg, track_pool=[0])
+    rng = np.random.default_rng(123)
+    shape = (wl.tokens_per_frame, wl.num_heads, wl.head_dim)
+    # a few distinct frames of bf16-pattern N(0,1)-like bits, reused
+    frames = []
+    for _ in range(4):
+        x = rng.standard_normal((2,) + shape).astype(np.float32)
+        frames.append((x.view(np.uint32) >> 16).astype(np.uint16))
+    sched = frame_schedule(wl, warm_frames + 1)
+    S, W = wl.scale_frames, wl.sliding_window
+
+    def one_frame(f, kind, attend_blocks):
+        kv = frames[f % 4]
+        if wl.dynamic or kind == "transient":
+            o.set_defer_eviction(True)
+        for b in range(wl.num_blocks):
+            o.append_frame(b, kv[0] if b == 0 else None, kv[1] if b == 0 else None)
+            o.evict_frames(b, S, W)
+            if b == 0:
+                o.plan()
+            pl = o.check_run(b)
+            if b < attend_blocks:
+                q = frames[(f + b) % 4][0]
+                paged_attention(o.pools[0], pl, cfg, q, wl.head_dim ** -0.5)
+        for b in range(wl.num_blocks):
+            if kind in ("transient", "reject"):
+                o.rollback_last_frame(b)
+            elif kind == "accept":
+                o.execute_deferred_eviction(b, S, W)
+        if kind == "transient":
+            o.set_defer_eviction(False)
+
+    for f in range(warm_frames):
+        one_frame(f, sched[f], 0)
+    f = warm_frames
+    t0 = time.perf_counter()
+    one_frame(f, "key", 0)          # the host steps of a frame, all blocks
+    t_host = time.perf_counter() - t0
+    o2 = None
+    t0 = time.perf_counter()
+    pl = o.plan()
+    for b in range(n_blocks_timed):
+        q = frames[b % 4][0]
+        paged_attention(o.pools[0], pl, cfg, q, wl.head_dim ** -0.5)
+    t_attn = (time.perf_counter() - t0) / n_blocks_timed
+    per_frame = t_host + t_attn * wl.num_blocks
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": 1.0 / per_frame,
+        "unit": "frames/s",
+        "cores": int(max(1, min(cores, blas))),
+        "kind": "oracle",
+        "sample": (f"one steady-state frame (frame {f}) of {wl.name}: page-pool "
+                   f"steps on all {wl.num_blocks} blocks ({t_host*1e3:.1f} ms) + "
+                   f"float64 dense attention of {n_blocks_timed} blocks, all "
+                   f"{wl.tokens_per_frame} rows x {wl.num_heads} heads over "
+                   f"{pl.num_visible_tokens(cfg)} visible tokens "
+                   f"({t_attn:.2f} s per block), scaled to {wl.num_blocks} blocks; "
+                   f"host cores {cores}, BLAS threads {blas}"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import streaming_paged_kv_amd as spkv
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    cache = spkv.PagedKVCache(**wl.cfg_kwargs(), device=dev)
+    nb = wl.num_blocks
+    S, W = wl.scale_frames, wl.sliding_window
+    total = args.warmup + args.steps
+    sched = frame_schedule(wl, total)
+
+    # input bank, resident in HBM before timing
+    nbank = max(1, min(args.bank, total))
+    bank = [[synth.frame_qkv(wl, f, b, device=dev) for b in range(nb)]
+            for f in range(nbank)]
+    outs = [torch.empty((wl.tokens_per_frame, wl.num_heads, wl.head_dim),
+                        dtype=torch.bfloat16, device=dev) for _ in range(nb)]
+    sm = wl.head_dim ** -0.5
+    hd = wl.num_heads * wl.head_dim
+    nq = wl.tokens_per_frame
+
+    use_ev = not args.no_events
+    ev_attn, ev_app = [], []
+    flops, app_bytes = [], []
+
+    def step(f, record):
+        kind = sched[f]
+        qkv = bank[f % nbank]
+        if wl.dynamic or kind == "transient":
+            cache.set_defer_eviction(True)
+        nk = None
+        for b in range(nb):
+            q, k, v = qkv[b]
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            cache.append_frame(b, k, v, stream=stream)
+            if record:
+                e1.record(stream)
+                ev_app.append((e0, e1))
+                app_bytes.append(8 * nq * hd)
+            cache.evict_frames(b, S, W)
+            if b == 0:
+                cache.plan(stream=stream)
+                if record:
+                    tab, npatch, lpl = cache.get_plan()
+                    nsp = len(tab) - npatch
+                    nk = (npatch * wl.patch_tokens +
+                          (nsp - 1) * wl.num_special_tokens *
+                          (wl.page_size // wl.num_special_tokens) + lpl)
+            if record:
+                a0 = torch.cuda.Event(enable_timing=True)
+                a1 = torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+            cache.run(b, q, out=outs[b], sm_scale=sm, stream=stream)
+            if record:
+                a1.record(stream)
+                ev_attn.append((a0, a1))
+                flops.append(4.0 * nq * nk * hd)
+        for b in range(nb):
+            if kind in ("transient", "reject"):
+                cache.rollback_last_frame(b)
+            elif kind == "accept":
+                cache.execute_deferred_eviction(b, S, W)
+        if kind == "transient":
+            cache.set_defer_eviction(False)
+
+    for f in range(args.warmup):
+        step(f, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for f in range(args.warmup, total):
+        step(f, use_ev)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+
+    result = {
+        "metric": METRIC,
+        "value": args.steps / dt,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl.name}: {nb} blocks, H={wl.num_heads}, D={wl.head_dim}, "
+                         f"page_size={wl.page_size}, {wl.patch_tokens} patch + "
+                         f"{wl.num_special_tokens} special tokens/frame, "
+                         f"S/W/R={wl.scale_frames}/{wl.sliding_window}/{wl.headroom}, "
+                         f"keyframe_interval={wl.keyframe_interval}"
+                         + (", dynamic accept/rollback" if wl.dynamic else "")),
+            "frames_timed": f"{args.warmup}..{total - 1}",
+            "input_bank_frames": nbank,
+        },
+    }
+    if use_ev:
+        t_attn = [a.elapsed_time(b) * 1e-3 for a, b in ev_attn]
+        t_app = [a.elapsed_time(b) * 1e-3 for a, b in ev_app]
+        avg_attn = sum(t_attn) / len(t_attn)
+        achieved = sum(flops) / sum(t_attn) / 1e12
+        avg_flops = sum(flops) / len(flops)
+        result["roofline"] = {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "kernel": "attn_kernel (+ split merge) per run()",
+            "avg_launch_us": avg_attn * 1e6,
+            "algorithmic_flops_per_launch": avg_flops,
+        }
+        app_gbs = sum(app_bytes) / sum(t_app) / 1e9
+        result["append"] = {
+            "bound": "hbm", "achieved": app_gbs, "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": app_gbs / PEAK_HBM_GBS,
+            "avg_launch_us": sum(t_app) / len(t_app) * 1e6,
+            "bytes_per_launch": app_bytes[0],
+        }
+    cache.close()
+    del bank
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.warmup, args.cpu_blocks)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

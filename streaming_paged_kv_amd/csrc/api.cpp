@@ -1,0 +1,440 @@
+// C ABI of libspkv.so: argument checks, the host allocator, the plan's
+// host-to-device copy and the kernel launches.  See include/spkv.h for the
+// contract of every call.
+#include "../../include/spkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+#include "pool.h"
+
+namespace {
+
+constexpr int kMaxSplits = 32;
+constexpr int64_t kAlign = 256;
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool to_geometry(const spkv_config* c, spkv::Geometry* g) {
+  if (!c) return false;
+  *g = spkv::Geometry{};
+  g->num_blocks = c->num_blocks;
+  g->num_heads = c->num_heads;
+  g->head_dim = c->head_dim;
+  g->page_size = c->page_size;
+  g->patch_tokens = c->patch_tokens;
+  g->num_special = c->num_special_tokens;
+  g->scale_frames = c->scale_frames;
+  g->sliding_window = c->sliding_window;
+  g->headroom = c->headroom;
+  g->max_total_frames = c->max_total_frames;
+  if (!g->derive()) return false;
+  // Element offsets are computed in 64 bits, but a page's token count times
+  // H*D and the visible token count must stay in int32 inside the kernels.
+  const int64_t hd = int64_t(g->num_heads) * g->head_dim;
+  if (hd > (1 << 20) || int64_t(g->page_size) * hd > (int64_t(1) << 31))
+    return false;
+  if (int64_t(g->max_num_pages) * g->page_size > (int64_t(1) << 30))
+    return false;
+  return true;
+}
+
+struct Sizes {
+  int64_t max_num_pages, pool_bytes, table_bytes, min_ws, per_split, full_ws;
+};
+
+Sizes sizes_of(const spkv::Geometry& g) {
+  Sizes s;
+  s.max_num_pages = g.max_num_pages;
+  s.pool_bytes = int64_t(g.max_num_pages) * 2 * g.page_size * g.num_heads *
+                 g.head_dim * 2;
+  s.table_bytes = round_up(int64_t(g.max_num_pages) * 4, kAlign);
+  s.min_ws = 2 * s.table_bytes;
+  // Partial O (fp32, D per row) and (m, l) for every (query, head) row.
+  const int64_t rows = int64_t(g.tokens_per_frame) * g.num_heads;
+  s.per_split = round_up(rows * g.head_dim * 4, kAlign) + round_up(rows * 8, kAlign);
+  s.full_ws = s.min_ws + kMaxSplits * s.per_split;
+  return s;
+}
+
+int status(spkv::Status s) { return static_cast<int>(s); }
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// Makes the handle's device current for the duration of a call.
+class DeviceGuard {
+ public:
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev_) == hipSuccess && prev_ != dev)
+      switched_ = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (switched_) (void)hipSetDevice(prev_);
+  }
+
+ private:
+  int prev_ = 0;
+  bool switched_ = false;
+};
+
+}  // namespace
+
+struct spkv_handle {
+  spkv::Geometry g{};
+  Sizes sz{};
+  std::unique_ptr<spkv::PagePool> pool;
+  bool host_only = true;
+  int device = 0;
+  std::vector<void*> pools;
+  char* ws = nullptr;
+  int64_t ws_bytes = 0;
+  int32_t* dev_table[2] = {nullptr, nullptr};
+  int32_t* stage = nullptr;          // pinned, 2 x max_num_pages
+  hipEvent_t copied[2] = {nullptr, nullptr};
+  bool copy_pending[2] = {false, false};
+  int plan_slot = 0;                 // slot holding the current plan
+  int next_slot = 0;
+  char* partials = nullptr;
+  int max_splits = 1;                // what the workspace holds
+  int forced_splits = 0;
+  int num_cus = 256;
+};
+
+extern "C" {
+
+SPKV_API const char* spkv_error_string(int code) {
+  switch (code) {
+    case SPKV_OK: return "ok";
+    case SPKV_ERR_INVALID_ARG: return "invalid argument";
+    case SPKV_ERR_BAD_BLOCK: return "block index out of range";
+    case SPKV_ERR_POOL_EXHAUSTED: return "no free patch page";
+    case SPKV_ERR_SPECIAL_OVERFLOW: return "special stream full";
+    case SPKV_ERR_NOTHING_TO_ROLLBACK: return "nothing to roll back";
+    case SPKV_ERR_EMPTY: return "no frame to plan";
+    case SPKV_ERR_NOT_PLANNED: return "run before plan";
+    case SPKV_ERR_STALE_PLAN: return "block state differs from the plan";
+    case SPKV_ERR_UNSUPPORTED: return "unsupported";
+    case SPKV_ERR_HIP: return "HIP runtime error";
+    case SPKV_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+SPKV_API int spkv_query_sizes(const spkv_config* cfg, int64_t* max_num_pages,
+                              int64_t* pool_bytes_per_block,
+                              int64_t* min_workspace_bytes,
+                              int64_t* full_workspace_bytes) {
+  spkv::Geometry g;
+  if (!to_geometry(cfg, &g)) return SPKV_ERR_INVALID_ARG;
+  if (g.head_dim != 64) return SPKV_ERR_UNSUPPORTED;
+  const Sizes s = sizes_of(g);
+  if (max_num_pages) *max_num_pages = s.max_num_pages;
+  if (pool_bytes_per_block) *pool_bytes_per_block = s.pool_bytes;
+  if (min_workspace_bytes) *min_workspace_bytes = s.min_ws;
+  if (full_workspace_bytes) *full_workspace_bytes = s.full_ws;
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_create(const spkv_config* cfg, void* const* pool_ptrs,
+                         void* workspace, int64_t workspace_bytes,
+                         spkv_handle** out) {
+  if (!out) return SPKV_ERR_INVALID_ARG;
+  *out = nullptr;
+  spkv::Geometry g;
+  if (!to_geometry(cfg, &g)) return SPKV_ERR_INVALID_ARG;
+  if (g.head_dim != 64) return SPKV_ERR_UNSUPPORTED;
+  const bool host_only = pool_ptrs == nullptr;
+  if (host_only != (workspace == nullptr)) return SPKV_ERR_INVALID_ARG;
+  const Sizes sz = sizes_of(g);
+  if (!host_only) {
+    for (int b = 0; b < g.num_blocks; ++b)
+      if (!pool_ptrs[b] || !aligned16(pool_ptrs[b])) return SPKV_ERR_INVALID_ARG;
+    if (!aligned16(workspace)) return SPKV_ERR_INVALID_ARG;
+    if (workspace_bytes < sz.min_ws) return SPKV_ERR_WORKSPACE;
+  }
+
+  std::unique_ptr<spkv_handle> h(new (std::nothrow) spkv_handle());
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  h->g = g;
+  h->sz = sz;
+  h->host_only = host_only;
+  try {
+    h->pool.reset(new spkv::PagePool(g));
+  } catch (...) {
+    return SPKV_ERR_INVALID_ARG;
+  }
+  if (host_only) {
+    *out = h.release();
+    return SPKV_OK;
+  }
+
+  if (hipGetDevice(&h->device) != hipSuccess) return SPKV_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, h->device) == hipSuccess)
+    h->num_cus = prop.multiProcessorCount;
+  h->pools.assign(pool_ptrs, pool_ptrs + g.num_blocks);
+  h->ws = static_cast<char*>(workspace);
+  h->ws_bytes = workspace_bytes;
+  h->dev_table[0] = reinterpret_cast<int32_t*>(h->ws);
+  h->dev_table[1] = reinterpret_cast<int32_t*>(h->ws + sz.table_bytes);
+  h->partials = h->ws + 2 * sz.table_bytes;
+  const int64_t room = workspace_bytes - 2 * sz.table_bytes;
+  h->max_splits = static_cast<int>(
+      std::max<int64_t>(1, std::min<int64_t>(kMaxSplits, room / sz.per_split)));
+  if (hipHostMalloc(reinterpret_cast<void**>(&h->stage),
+                    size_t(2) * g.max_num_pages * sizeof(int32_t),
+                    hipHostMallocDefault) != hipSuccess) {
+    h->stage = nullptr;
+    return SPKV_ERR_HIP;
+  }
+  for (int i = 0; i < 2; ++i) {
+    if (hipEventCreateWithFlags(&h->copied[i], hipEventDisableTiming) !=
+        hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(h->copied[j]);
+      (void)hipHostFree(h->stage);
+      return SPKV_ERR_HIP;
+    }
+  }
+  *out = h.release();
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_destroy(spkv_handle* h) {
+  if (!h) return SPKV_OK;
+  int rc = SPKV_OK;
+  if (!h->host_only) {
+    DeviceGuard guard(h->device);
+    for (int i = 0; i < 2; ++i) {
+      if (h->copy_pending[i] && hipEventSynchronize(h->copied[i]) != hipSuccess)
+        rc = SPKV_ERR_HIP;
+      if (h->copied[i]) (void)hipEventDestroy(h->copied[i]);
+    }
+    if (h->stage) (void)hipHostFree(h->stage);
+  }
+  delete h;
+  return rc;
+}
+
+SPKV_API int spkv_append_frame(spkv_handle* h, int32_t block, const void* k,
+                               const void* v, void* hip_stream) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  if (block < 0 || block >= h->g.num_blocks) return SPKV_ERR_BAD_BLOCK;
+  if (h->host_only) {
+    if (k || v) return SPKV_ERR_INVALID_ARG;
+  } else {
+    if (!k || !v || !aligned16(k) || !aligned16(v)) return SPKV_ERR_INVALID_ARG;
+  }
+  spkv::AppendResult r;
+  const spkv::Status s = h->pool->append(block, &r);
+  if (s != spkv::Status::ok) return status(s);
+  if (h->host_only) return SPKV_OK;
+
+  DeviceGuard guard(h->device);
+  const spkv::Geometry& g = h->g;
+  const int64_t hd = int64_t(g.num_heads) * g.head_dim;
+  const int64_t page = int64_t(g.page_size) * hd;
+  spkv::AppendArgs a;
+  a.k = k;
+  a.v = v;
+  a.pool = h->pools[block];
+  a.patch_k_off = (int64_t(r.patch_page) * 2 + 0) * page;
+  a.patch_v_off = (int64_t(r.patch_page) * 2 + 1) * page;
+  a.special_k_off = (int64_t(r.special_page) * 2 + 0) * page + int64_t(r.special_slot) * hd;
+  a.special_v_off = (int64_t(r.special_page) * 2 + 1) * page + int64_t(r.special_slot) * hd;
+  a.patch_elems = int64_t(g.patch_tokens) * hd;
+  a.special_elems = int64_t(g.num_special) * hd;
+  if (spkv::launch_append(a, static_cast<hipStream_t>(hip_stream)) != hipSuccess) {
+    h->pool->undo_append(block, r);
+    return SPKV_ERR_HIP;
+  }
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_evict_frames(spkv_handle* h, int32_t block,
+                               int32_t scale_frames, int32_t sliding_window,
+                               int32_t cross_frame_special,
+                               int32_t camera_only) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  return status(h->pool->evict(block, scale_frames, sliding_window,
+                               cross_frame_special, camera_only, nullptr));
+}
+
+SPKV_API int spkv_set_defer_eviction(spkv_handle* h, int32_t enable) {
+  if (!h || (enable != 0 && enable != 1)) return SPKV_ERR_INVALID_ARG;
+  h->pool->set_defer(enable == 1);
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_execute_deferred_eviction(spkv_handle* h, int32_t block,
+                                            int32_t scale_frames,
+                                            int32_t sliding_window) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  return status(
+      h->pool->execute_deferred(block, scale_frames, sliding_window, nullptr));
+}
+
+SPKV_API int spkv_rollback_last_frame(spkv_handle* h, int32_t block) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  return status(h->pool->rollback(block));
+}
+
+SPKV_API int spkv_reset(spkv_handle* h) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  h->pool->reset();
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  if (h->host_only) return status(h->pool->plan());
+  DeviceGuard guard(h->device);
+  // The staging slot is reused every other plan: its previous copy must have
+  // left the host buffer before it is overwritten.
+  const int slot = h->next_slot;
+  if (h->copy_pending[slot]) {
+    if (hipEventSynchronize(h->copied[slot]) != hipSuccess) return SPKV_ERR_HIP;
+    h->copy_pending[slot] = false;
+  }
+  const spkv::Status s = h->pool->build_plan();
+  if (s != spkv::Status::ok) return status(s);
+  const spkv::PlanView pv = h->pool->pending_view();
+  int32_t* host = h->stage + size_t(slot) * h->g.max_num_pages;
+  std::memcpy(host, pv.table, size_t(pv.n_pages) * sizeof(int32_t));
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (hipMemcpyAsync(h->dev_table[slot], host, size_t(pv.n_pages) * sizeof(int32_t),
+                     hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipEventRecord(h->copied[slot], st) != hipSuccess) {
+    return SPKV_ERR_HIP;  // the pending plan is simply not committed
+  }
+  h->pool->commit_plan();
+  h->copy_pending[slot] = true;
+  h->plan_slot = slot;
+  h->next_slot = slot ^ 1;
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_set_num_splits(spkv_handle* h, int32_t num_splits) {
+  if (!h || num_splits < 0) return SPKV_ERR_INVALID_ARG;
+  h->forced_splits = num_splits;
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
+                      int32_t nq, float sm_scale, void* hip_stream) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  if (block < 0 || block >= h->g.num_blocks) return SPKV_ERR_BAD_BLOCK;
+  const spkv::Geometry& g = h->g;
+  if (nq < 1 || nq > g.tokens_per_frame || !std::isfinite(sm_scale) ||
+      !(sm_scale > 0.0f))
+    return SPKV_ERR_INVALID_ARG;
+  if (h->host_only) {
+    if (q || out) return SPKV_ERR_INVALID_ARG;
+  } else {
+    if (!q || !out || !aligned16(q) || !aligned16(out)) return SPKV_ERR_INVALID_ARG;
+    const size_t bytes = size_t(nq) * g.num_heads * g.head_dim * 2;
+    const char* qb = static_cast<const char*>(q);
+    const char* ob = static_cast<const char*>(out);
+    if (qb < ob + bytes && ob < qb + bytes) return SPKV_ERR_INVALID_ARG;
+  }
+  const spkv::Status s = h->pool->check_run(block);
+  if (s != spkv::Status::ok) return status(s);
+  if (h->host_only) return SPKV_ERR_UNSUPPORTED;
+
+  const spkv::PlanView pv = h->pool->plan_view();
+  const int64_t nk = pv.visible_tokens;
+  const int64_t n_ktiles = (nk + spkv::kAttnKeyTile - 1) / spkv::kAttnKeyTile;
+  const int64_t n_qtiles = (nq + spkv::kAttnQueryTile - 1) / spkv::kAttnQueryTile;
+  int64_t splits;
+  if (h->forced_splits > 0) {
+    splits = h->forced_splits;
+  } else {
+    // Two resident workgroups per CU; each split keeps >= 4 key tiles.
+    const int64_t want = 2 * int64_t(h->num_cus);
+    const int64_t units = n_qtiles * g.num_heads;
+    splits = (want + units - 1) / units;
+    splits = std::min<int64_t>(splits, std::max<int64_t>(1, n_ktiles / 4));
+  }
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, h->max_splits));
+  splits = std::min<int64_t>(splits, n_ktiles);
+  const int64_t tiles_per_split = (n_ktiles + splits - 1) / splits;
+  splits = (n_ktiles + tiles_per_split - 1) / tiles_per_split;  // none empty
+
+  DeviceGuard guard(h->device);
+  spkv::AttnArgs a;
+  a.pool = static_cast<const uint16_t*>(h->pools[block]);
+  a.table = h->dev_table[h->plan_slot];
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = static_cast<uint16_t*>(out);
+  const int64_t rows = int64_t(nq) * g.num_heads;
+  a.part_o = reinterpret_cast<float*>(h->partials);
+  a.part_ml = reinterpret_cast<float*>(
+      h->partials + round_up(rows * g.head_dim * 4 * splits, kAlign));
+  a.nq = nq;
+  a.num_heads = g.num_heads;
+  a.page_size = g.page_size;
+  a.patch_len = g.patch_tokens;
+  a.special_len = g.num_special * g.frames_per_spage;
+  a.n_patch = pv.n_patch;
+  a.n_pages = pv.n_pages;
+  a.last_len = pv.last_page_len;
+  a.nk = static_cast<int32_t>(nk);
+  a.splits = static_cast<int32_t>(splits);
+  a.tokens_per_split = static_cast<int32_t>(tiles_per_split * spkv::kAttnKeyTile);
+  a.sm_scale = sm_scale;
+  if (spkv::launch_attention(a, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    return SPKV_ERR_HIP;
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_get_cache_stats(const spkv_handle* h, int32_t block,
+                                  spkv_stats* out) {
+  if (!h || !out) return SPKV_ERR_INVALID_ARG;
+  spkv::PagePool::Stats s;
+  const spkv::Status st = h->pool->stats(block, &s);
+  if (st != spkv::Status::ok) return status(st);
+  out->frame_count = s.frames;
+  out->scale_pages = s.scale;
+  out->live_pages = s.live;
+  out->free_pages = s.free_pages;
+  out->reserved = 0;
+  out->special_tokens = s.special_tokens;
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_get_plan(const spkv_handle* h, int32_t* table, int32_t cap,
+                           int32_t* n_pages, int32_t* n_patch_pages,
+                           int32_t* last_page_len) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  if (!h->pool->planned()) return SPKV_ERR_NOT_PLANNED;
+  const spkv::PlanView pv = h->pool->plan_view();
+  if (table) {
+    if (cap < pv.n_pages) return SPKV_ERR_INVALID_ARG;
+    std::memcpy(table, pv.table, size_t(pv.n_pages) * sizeof(int32_t));
+  }
+  if (n_pages) *n_pages = pv.n_pages;
+  if (n_patch_pages) *n_patch_pages = pv.n_patch;
+  if (last_page_len) *last_page_len = pv.last_page_len;
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_get_block_state(const spkv_handle* h, int32_t block,
+                                  int32_t* scale, int32_t* live,
+                                  int32_t* free_list, int32_t cap,
+                                  int32_t* n_scale, int32_t* n_live,
+                                  int32_t* n_free, int64_t* n_special_frames) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  return status(h->pool->block_state(block, scale, live, free_list, cap, n_scale,
+                                     n_live, n_free, n_special_frames));
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Launch wrappers of the gfx950 kernels (internal to libspkv.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace spkv {
+
+// Work of one append: four contiguous runs of 16-byte chunks.
+struct AppendArgs {
+  const void* k;          // [tokens_per_frame][H][D] bf16
+  const void* v;
+  void* pool;             // block's pool base
+  int64_t patch_k_off;    // element offsets into the pool
+  int64_t patch_v_off;
+  int64_t special_k_off;
+  int64_t special_v_off;
+  int64_t patch_elems;    // patch_tokens * H * D
+  int64_t special_elems;  // num_special * H * D
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+// One attention run over a planned page table.
+struct AttnArgs {
+  const uint16_t* pool;     // block's pool (bf16 bits)
+  const int32_t* table;     // device page table, n_pages entries
+  const uint16_t* q;        // [nq][H][D]
+  uint16_t* out;            // [nq][H][D]
+  float* part_o;            // [splits][nq][H][D]     (splits > 1)
+  float* part_ml;           // [splits][nq][H][2]     (splits > 1)
+  int32_t nq, num_heads, page_size;
+  int32_t patch_len;        // valid tokens of a patch page
+  int32_t special_len;      // valid tokens of a full special page
+  int32_t n_patch, n_pages, last_len;
+  int32_t nk;               // visible tokens
+  int32_t splits, tokens_per_split;
+  float sm_scale;
+};
+
+// Key tiles the kernel uses; run() sizes the split from it.
+constexpr int kAttnKeyTile = 64;
+constexpr int kAttnQueryTile = 256;
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace spkv

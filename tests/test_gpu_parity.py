@@ -1,0 +1,315 @@
+"""Parity of the HIP path (through the C ABI) with the oracle on the GPU.
+
+Bar: page tables, last_page_len, stats and allocator state bit-exact at every
+frame; pool bytes bit-exact (whole pool on small streams; the visible patch
+pages and every special page at chosen frames on full-size streams);
+attention within max-abs 2e-2 and mean-abs 2e-3 of the float64 oracle, with
+relative L2 error <= 1e-2 as an extra guard."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import harness as H
+from oracle import OracleConfig, PagePoolOracle, bf16_bits_to_f64
+from oracle.attention import paged_attention, dense_attention
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def new_cache(wl, **kw):
+    import streaming_paged_kv_amd as spkv
+    return spkv.PagedKVCache(**wl.cfg_kwargs(), **kw)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------ small streams
+def full_parity(wl, frames=None, splits=0):
+    """Every frame: whole-pool bytes, plan, stats, state bit-exact; attention
+    on every row of every block."""
+    need_gpu()
+    cache = new_cache(wl)
+    if splits:
+        cache.set_num_splits(splits)
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    o = PagePoolOracle(cfg, track_pool=range(wl.num_blocks))
+    kinds = H.frame_kinds(wl, frames)
+    sm = wl.head_dim ** -0.5
+    worst = 0.0
+    for f, (kind, reset) in enumerate(kinds):
+        qkv = H.gen_frame(wl, f, wl.num_blocks, DEV)
+        bits = [[synth.bf16_bits(t) for t in x] for x in qkv]
+        outs = [torch.empty_like(x[0]) for x in qkv]
+        # oracle first so that its attention uses the state of this frame
+        ref = {}
+
+        def on_plan(oo):
+            pass
+
+        S, W = wl.scale_frames, wl.sliding_window
+        if reset:
+            o.reset()
+        if wl.dynamic or kind == "transient":
+            o.set_defer_eviction(True)
+        for b in range(wl.num_blocks):
+            o.append_frame(b, bits[b][1], bits[b][2])
+            o.evict_frames(b, S, W)
+            if b == 0:
+                o.plan()
+            pl = o.check_run(b)
+            ref[b] = paged_attention(o.pools[b], pl, cfg, bits[b][0], sm)
+        plan_ref = (list(o.plan_state.table), o.plan_state.n_patch,
+                    o.plan_state.last_page_len)
+        for b in range(wl.num_blocks):
+            if kind in ("transient", "reject"):
+                o.rollback_last_frame(b)
+            elif kind == "accept":
+                o.execute_deferred_eviction(b, S, W)
+        if kind == "transient":
+            o.set_defer_eviction(False)
+
+        H.gpu_step(cache, wl, kind, reset, qkv, outs)
+        torch.cuda.synchronize()
+        assert cache.get_plan() == plan_ref, f
+        for b in range(wl.num_blocks):
+            assert list(o.block_state(b)) == list(cache.get_block_state(b)), (f, b)
+            assert tuple(o.get_cache_stats(b)) == cache.get_cache_stats(b), (f, b)
+            assert np.array_equal(synth.bf16_bits(cache.pools[b]), o.pools[b]), (f, b)
+            mx, mean, rel = H.compare(outs[b], ref[b], (wl.name, f, b))
+            worst = max(worst, mx)
+    cache.close()
+    return worst
+
+
+def test_tiny_stream_every_frame():
+    log("tiny stream, 12 keyframes")
+    full_parity(synth.WORKLOADS["tiny"])
+
+
+def test_tiny_stream_interval_reset_and_rollback():
+    wl = synth.WORKLOADS["tiny"].with_(keyframe_interval=2, frames=14, reset_every=9)
+    log("tiny stream, interval 2, reset at 9")
+    full_parity(wl)
+    wl2 = synth.WORKLOADS["tiny"].with_(dynamic=True, frames=20, seed=11)
+    log("tiny stream, dynamic accept/rollback")
+    full_parity(wl2)
+
+
+MID = synth.Workload("mid-ragged", 2, 16, 64, 203, 200, 6, 2, 6, 2, 64, 16,
+                     keyframe_interval=2, seed=21)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 7])
+def test_mid_stream_ragged_pages_and_splits(splits):
+    """200 patch tokens in 203-token pages, 33 frames per special page: tiles
+    cross pages at varying offsets; forced key-range splits."""
+    log(f"mid stream, splits={splits}")
+    full_parity(MID, splits=splits)
+
+
+BIGQ = synth.Workload("bigq", 1, 16, 64, 999, 999, 6, 1, 2, 1, 400, 6,
+                      keyframe_interval=2, k_scale=0.5, seed=22)
+
+
+def test_many_query_tiles_and_ragged_query_tail():
+    """1005 query rows = 3 full 256-row tiles plus a 237-row tail."""
+    log("1005 queries, 999-token pages")
+    full_parity(BIGQ)
+
+
+def test_exact_and_padded_pages_give_identical_outputs():
+    """The same token stream in 999- and 1024-token pages: the kernel walks
+    the same token sequence, so the outputs are bit-identical."""
+    need_gpu()
+    a = BIGQ.with_(name="exact", frames=5)
+    b = BIGQ.with_(name="padded", page_size=1024, frames=5)
+    ca, cb = new_cache(a), new_cache(b)
+    for c in (ca, cb):
+        c.set_num_splits(3)
+    for f, (kind, reset) in enumerate(H.frame_kinds(a)):
+        qkv = H.gen_frame(a, f, 1, DEV)
+        oa = [torch.empty_like(qkv[0][0])]
+        ob = [torch.empty_like(qkv[0][0])]
+        H.gpu_step(ca, a, kind, reset, qkv, oa)
+        H.gpu_step(cb, b, kind, reset, qkv, ob)
+        torch.cuda.synchronize()
+        assert torch.equal(oa[0], ob[0]), f
+    ca.close()
+    cb.close()
+
+
+# ----------------------------------------------------------- edge cases
+def test_edge_cases_nq_scale_and_sharp_keys():
+    need_gpu()
+    wl = MID.with_(name="edge", num_blocks=1, frames=6, keyframe_interval=1)
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    o = PagePoolOracle(cfg, track_pool=[0])
+    cache = new_cache(wl)
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    for f in range(wl.frames):
+        q, k, v = synth.frame_qkv(wl, f, 0, device=DEV)
+        if f == 3:
+            # plant: key of patch token 17 is a large multiple of query 0's
+            k = k.clone()
+            k[6 + 17] = (q[0].float() * 4.0).to(torch.bfloat16)
+        cache.append_frame(0, k, v)
+        cache.evict_frames(0, wl.scale_frames, wl.sliding_window)
+        cache.plan()
+        o.append_frame(0, synth.bf16_bits(k), synth.bf16_bits(v))
+        o.evict_frames(0, wl.scale_frames, wl.sliding_window)
+        pl = o.plan()
+        qb = synth.bf16_bits(q)
+        for nq, sm in ((1, 0.125), (7, 1.0), (wl.tokens_per_frame, 0.02),
+                       (33, 0.125)):
+            out = cache.run(0, q[:nq].contiguous(), sm_scale=sm)
+            torch.cuda.synchronize()
+            ref = paged_attention(o.pools[0], pl, cfg, qb[:nq], sm)
+            H.compare(out, ref, ("edge", f, nq, sm))
+    # constant V over all visible tokens gives that constant
+    cache.close()
+
+
+def test_constant_v_is_reproduced():
+    need_gpu()
+    wl = MID.with_(name="constv", num_blocks=1, frames=4, keyframe_interval=1)
+    cache = new_cache(wl)
+    cvec = torch.randn(16, 64, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    for f in range(wl.frames):
+        q, k, _ = synth.frame_qkv(wl, f, 0, device=DEV)
+        v = cvec.to(DEV).expand(wl.tokens_per_frame, 16, 64).contiguous()
+        cache.append_frame(0, k, v)
+        cache.evict_frames(0, wl.scale_frames, wl.sliding_window)
+        cache.plan()
+        out = cache.run(0, q)
+        torch.cuda.synchronize()
+        want = cvec.double().numpy()[None].repeat(wl.tokens_per_frame, 0)
+        H.compare(out, want, ("constv", f))
+    cache.close()
+
+
+# ------------------------------------------------------- full-size streams
+def full_size(name, num_blocks=None, attn_blocks=(0, 11, 23), pool_blocks=(0, 23),
+              frames=None, milestone_keys=None):
+    """The workload's whole stream on the GPU, with the oracle checking every
+    plan and state bit-exact, and at milestone frames the attention of
+    sampled rows (all heads) and the bytes of the visible pages."""
+    need_gpu()
+    wl = synth.WORKLOADS[name]
+    if num_blocks is not None:
+        wl = wl.with_(num_blocks=num_blocks)
+    nb = wl.num_blocks
+    attn_blocks = [b for b in attn_blocks if b < nb]
+    pool_blocks = [b for b in pool_blocks if b < nb]
+    kinds, plans, writers_at, ms = H.dry_run(wl, frames)
+    milestones = sorted(set(ms.values()))
+    need = H.needed_frames(wl, plans, writers_at, milestones)
+    log(f"{name}: {len(kinds)} frames, {nb} blocks, milestones {ms}")
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    tracked = sorted(set(attn_blocks) | set(pool_blocks))
+    o = PagePoolOracle(cfg, track_pool=tracked)
+    cache = new_cache(wl)
+    sm = wl.head_dim ** -0.5
+    ns = wl.num_special_tokens
+    rows = H.sample_rows(wl.tokens_per_frame)
+    outs = [torch.empty((wl.tokens_per_frame, wl.num_heads, wl.head_dim),
+                        dtype=torch.bfloat16, device=DEV) for _ in range(nb)]
+    checked = 0
+    for f, (kind, reset) in enumerate(kinds):
+        qkv = H.gen_frame(wl, f, nb, DEV)
+
+        def kv_of(b):
+            if b not in tracked:
+                return None, None
+            k, v = qkv[b][1], qkv[b][2]
+            if f in need:
+                return synth.bf16_bits(k), synth.bf16_bits(v)
+            kb = np.zeros((wl.tokens_per_frame, wl.num_heads, wl.head_dim), np.uint16)
+            vb = kb.copy()
+            kb[:ns] = synth.bf16_bits(k[:ns])
+            vb[:ns] = synth.bf16_bits(v[:ns])
+            return kb, vb
+
+        refs = {}
+        snap = {}
+
+        def on_plan(oo, f=f):
+            pass
+
+        # oracle side, capturing the attention references before rollback
+        S, W = wl.scale_frames, wl.sliding_window
+        if reset:
+            o.reset()
+        if wl.dynamic or kind == "transient":
+            o.set_defer_eviction(True)
+        for b in range(nb):
+            k, v = kv_of(b)
+            o.append_frame(b, k, v)
+            o.evict_frames(b, S, W)
+            if b == 0:
+                o.plan()
+            pl = o.check_run(b)
+            if f in milestones and b in attn_blocks:
+                refs[b] = paged_attention(o.pools[b], pl, cfg,
+                                          synth.bf16_bits(qkv[b][0]), sm, rows=rows)
+            if f in milestones and b in pool_blocks:
+                sp = pl.table[pl.n_patch:]
+                vis = pl.table[:pl.n_patch]
+                snap[b] = (vis, sp, o.pools[b][vis].copy(), o.pools[b][sp].copy())
+        plan_ref = (list(o.plan_state.table), o.plan_state.n_patch,
+                    o.plan_state.last_page_len)
+        for b in range(nb):
+            if kind in ("transient", "reject"):
+                o.rollback_last_frame(b)
+            elif kind == "accept":
+                o.execute_deferred_eviction(b, S, W)
+        if kind == "transient":
+            o.set_defer_eviction(False)
+
+        # HIP side
+        H.gpu_step(cache, wl, kind, reset, qkv, outs)
+        assert cache.get_plan() == plan_ref, f
+        if f in milestones:
+            torch.cuda.synchronize()
+            for b in range(nb):
+                assert list(o.block_state(b)) == list(cache.get_block_state(b)), (f, b)
+                assert tuple(o.get_cache_stats(b)) == cache.get_cache_stats(b), (f, b)
+            for b, (vis, sp, pv, ps) in snap.items():
+                gp = cache.pools[b]
+                assert np.array_equal(synth.bf16_bits(gp[vis]), pv), (f, b)
+                assert np.array_equal(synth.bf16_bits(gp[sp]), ps), (f, b)
+            for b, ref in refs.items():
+                got = outs[b][rows]
+                mx, mean, rel = H.compare(got, ref, (name, f, b))
+                checked += 1
+            log(f"  frame {f} checked (Nk={sum(plans[f][1:2])} pages)")
+    cache.close()
+    assert checked >= len(milestones)
+
+
+def test_full_224x224_stream():
+    full_size("224x224")
+
+
+def test_full_518x378_exact_stream():
+    full_size("518x378")
+
+
+def test_full_518x378_padded_long_stream():
+    # 4096 frames; three blocks (the kernel's launch shape depends on the
+    # query count, heads and visible tokens, not on the number of blocks)
+    full_size("518x378-padded", num_blocks=3, attn_blocks=(0, 2), pool_blocks=(0, 2))
+
+
+def test_full_dynamic_stream():
+    full_size("dynamic")

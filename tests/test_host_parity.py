@@ -1,0 +1,168 @@
+"""The C++ page-pool allocator (through the C ABI, host-only handles, no GPU)
+against the oracle's state machine: bit-exact block state, plans, stats and
+error codes on fixed and random operation sequences."""
+
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import streaming_paged_kv_amd as spkv
+from oracle import OracleConfig, OracleError, PagePoolOracle
+import synth
+
+
+def make_pair(**cfg):
+    o = PagePoolOracle(OracleConfig(**cfg))
+    c = spkv.PagedKVCache(host_only=True, **cfg)
+    return o, c
+
+
+def code_of(fn, *a):
+    try:
+        fn(*a)
+        return "OK"
+    except OracleError as e:
+        return e.name
+    except spkv.SpkvError as e:
+        return e.name
+
+
+def assert_same(o, c):
+    cfg = o.cfg
+    for b in range(cfg.num_blocks):
+        assert list(o.block_state(b)) == list(c.get_block_state(b)), b
+        assert tuple(o.get_cache_stats(b)) == c.get_cache_stats(b), b
+    if o.plan_state is None:
+        assert code_of(c.get_plan) == "NOT_PLANNED"
+    else:
+        pl = o.plan_state
+        assert c.get_plan() == (pl.table, pl.n_patch, pl.last_page_len)
+
+
+def step(o, c, op, block, arg):
+    cfg = o.cfg
+    if op == "append":
+        r = (code_of(o.append_frame, block), code_of(c.append_frame, block))
+    elif op == "evict":
+        w = arg if arg else cfg.sliding_window
+        r = (code_of(o.evict_frames, block, cfg.scale_frames, w),
+             code_of(c.evict_frames, block, cfg.scale_frames, w))
+    elif op == "evict_badS":
+        r = (code_of(o.evict_frames, block, cfg.scale_frames + 1, cfg.sliding_window),
+             code_of(c.evict_frames, block, cfg.scale_frames + 1, cfg.sliding_window))
+    elif op == "evict_flags":
+        r = (code_of(o.evict_frames, block, cfg.scale_frames, cfg.sliding_window, 0, 1),
+             code_of(c.evict_frames, block, cfg.scale_frames, cfg.sliding_window, 0, 1))
+    elif op == "defer":
+        r = (code_of(o.set_defer_eviction, bool(arg)),
+             code_of(c.set_defer_eviction, bool(arg)))
+    elif op == "execute":
+        w = arg if arg else cfg.sliding_window
+        r = (code_of(o.execute_deferred_eviction, block, cfg.scale_frames, w),
+             code_of(c.execute_deferred_eviction, block, cfg.scale_frames, w))
+    elif op == "rollback":
+        r = (code_of(o.rollback_last_frame, block), code_of(c.rollback_last_frame, block))
+    elif op == "reset":
+        r = (code_of(o.reset), code_of(c.reset))
+    elif op == "plan":
+        r = (code_of(o.plan), code_of(c.plan))
+    elif op == "run":
+        ro = code_of(o.check_run, block)
+        rc = code_of(c.run, block)
+        # a host-only handle reports UNSUPPORTED once the checks pass
+        r = (ro, "OK" if rc == "UNSUPPORTED" else rc)
+    else:
+        raise AssertionError(op)
+    assert r[0] == r[1], (op, block, arg, r)
+
+
+CFGS = [
+    dict(num_blocks=2, num_heads=4, head_dim=64, page_size=16, patch_tokens=16,
+         num_special_tokens=6, scale_frames=2, sliding_window=4, headroom=2,
+         max_total_frames=32),
+    dict(num_blocks=3, num_heads=1, head_dim=64, page_size=13, patch_tokens=11,
+         num_special_tokens=4, scale_frames=1, sliding_window=2, headroom=1,
+         max_total_frames=9),
+    dict(num_blocks=1, num_heads=2, head_dim=64, page_size=6, patch_tokens=6,
+         num_special_tokens=6, scale_frames=0, sliding_window=3, headroom=0,
+         max_total_frames=5),
+]
+
+op_strategy = st.tuples(
+    st.sampled_from(["append", "append", "append", "evict", "evict", "defer",
+                     "execute", "rollback", "plan", "plan", "run", "reset",
+                     "evict_badS", "evict_flags"]),
+    st.integers(-1, 3), st.integers(0, 6))
+
+
+@pytest.mark.parametrize("ci", range(len(CFGS)))
+@settings(max_examples=120, deadline=None)
+@given(ops=st.lists(op_strategy, min_size=1, max_size=80))
+def test_random_ops_match_oracle(ci, ops):
+    o, c = make_pair(**CFGS[ci])
+    try:
+        for op, block, arg in ops:
+            step(o, c, op, block, arg)
+            assert_same(o, c)
+    finally:
+        c.close()
+
+
+def test_tiny_stream_worked_example_through_abi(golden_dir):
+    import json, os
+    g = json.load(open(os.path.join(golden_dir, "tiny_stream_conventions.json")))
+    cfg = g["config"]
+    c = spkv.PagedKVCache(host_only=True, **cfg)
+    for row in g["frames"]:
+        c.append_frame(0)
+        c.evict_frames(0, cfg["scale_frames"], cfg["sliding_window"])
+        c.plan()
+        assert c.get_plan()[0] == row["table"]
+        assert c.get_plan()[2] == row["last_page_len"]
+        assert c.get_block_state(0)[2] == row["free"]
+        assert list(c.get_cache_stats(0)) == row["stats"]
+    c.close()
+
+
+@pytest.mark.parametrize("name", ["224x224", "518x378", "518x378-padded", "dynamic"])
+def test_full_stream_schedules_match_oracle(name):
+    """The whole frame schedule of each workload (all blocks, every frame),
+    bit-exact on every block's state and on every plan."""
+    wl = synth.WORKLOADS[name]
+    cfg = wl.cfg_kwargs()
+    o, c = make_pair(**cfg)
+    S, W = wl.scale_frames, wl.sliding_window
+    decisions = synth.accept_decisions(wl) if wl.dynamic else None
+    nb = wl.num_blocks
+    frames = min(wl.frames, 1200)
+    if wl.dynamic:
+        o.set_defer_eviction(True)
+        c.set_defer_eviction(True)
+    for f in range(frames):
+        if wl.reset_every and f > 0 and f % wl.reset_every == 0:
+            o.reset(); c.reset()
+            if wl.dynamic:
+                o.set_defer_eviction(True); c.set_defer_eviction(True)
+        key = synth.is_keyframe(wl, f)
+        transient = not wl.dynamic and not key
+        if transient:
+            o.set_defer_eviction(True); c.set_defer_eviction(True)
+        for b in range(nb):
+            o.append_frame(b); c.append_frame(b)
+            o.evict_frames(b, S, W); c.evict_frames(b, S, W)
+            if b == 0:
+                o.plan(); c.plan()
+                pl = o.plan_state
+                assert c.get_plan() == (pl.table, pl.n_patch, pl.last_page_len), f
+            o.check_run(b)
+            assert code_of(c.run, b) == "UNSUPPORTED"
+        for b in range(nb):
+            if transient or (wl.dynamic and not decisions[f]):
+                o.rollback_last_frame(b); c.rollback_last_frame(b)
+            elif wl.dynamic:
+                o.execute_deferred_eviction(b, S, W)
+                c.execute_deferred_eviction(b, S, W)
+        if transient:
+            o.set_defer_eviction(False); c.set_defer_eviction(False)
+        if f % 50 == 0 or f == frames - 1:
+            assert_same(o, c)
+    c.close()
