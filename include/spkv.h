@@ -102,8 +102,10 @@ typedef struct spkv_stats {
  *   max_num_pages        = M + ceil(max_total_frames / floor(page_size / ns))
  *   pool_bytes_per_block = max_num_pages * 2 * page_size * H * D * 2
  *   min_workspace_bytes  = the least device workspace create() accepts: the
- *                          double-buffered device page table.  run() then
- *                          processes each (query tile, head) in one pass.
+ *                          double-buffered device page table and its
+ *                          per-token expansion (4 bytes per page slot).
+ *                          run() then processes each (query tile, head) in
+ *                          one pass.
  *   full_workspace_bytes = workspace that lets run() split the key range
  *                          across as many workgroups as it wants (up to 32
  *                          splits, each needing (ns+P)*H*(D+2)*4 bytes of
@@ -179,9 +181,10 @@ SPKV_API int spkv_reset(spkv_handle* h);
 /* plan() once per frame step, from block 0 ([LB-KV] "Kernel-Level Execution
  * Flow"; [LB-PERF] "One-Time Planning Pattern"): visible page table scale ->
  * live window -> special pages and last_page_len, the valid tokens of the last
- * special page ([LB-KV] "Physical Page Layout and Indexing").  Enqueues one
- * small host-to-device copy of the table on hip_stream.  EMPTY if block 0
- * holds no frame. */
+ * special page ([LB-KV] "Physical Page Layout and Indexing").  Enqueues on
+ * hip_stream one small host-to-device copy of the table and one kernel that
+ * expands it into the pool row of every visible token, which run() reads.
+ * EMPTY if block 0 holds no frame. */
 SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream);
 
 /* run(block) ([LB-KV] "Kernel-Level Execution Flow"): for every query row i

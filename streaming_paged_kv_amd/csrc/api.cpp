@@ -48,7 +48,8 @@ bool to_geometry(const spkv_config* c, spkv::Geometry* g) {
 }
 
 struct Sizes {
-  int64_t max_num_pages, pool_bytes, table_bytes, min_ws, per_split, full_ws;
+  int64_t max_num_pages, pool_bytes, table_bytes, rowmap_entries,
+      rowmap_bytes, min_ws, per_split, full_ws;
 };
 
 Sizes sizes_of(const spkv::Geometry& g) {
@@ -57,7 +58,12 @@ Sizes sizes_of(const spkv::Geometry& g) {
   s.pool_bytes = int64_t(g.max_num_pages) * 2 * g.page_size * g.num_heads *
                  g.head_dim * 2;
   s.table_bytes = round_up(int64_t(g.max_num_pages) * 4, kAlign);
-  s.min_ws = 2 * s.table_bytes;
+  // Row map: at most every slot of every page is visible; rounded up to a
+  // key tile and padded.
+  s.rowmap_entries = round_up(int64_t(g.max_num_pages) * g.page_size,
+                              spkv::kAttnKeyTile) + spkv::kRowmapPad;
+  s.rowmap_bytes = round_up(s.rowmap_entries * 4, kAlign);
+  s.min_ws = 2 * s.table_bytes + 2 * s.rowmap_bytes;
   // Partial O (fp32, D per row) and (m, l) for every (query, head) row.
   const int64_t rows = int64_t(g.tokens_per_frame) * g.num_heads;
   s.per_split = round_up(rows * g.head_dim * 4, kAlign) + round_up(rows * 8, kAlign);
@@ -99,6 +105,7 @@ struct spkv_handle {
   char* ws = nullptr;
   int64_t ws_bytes = 0;
   int32_t* dev_table[2] = {nullptr, nullptr};
+  uint32_t* dev_rowmap[2] = {nullptr, nullptr};
   int32_t* stage = nullptr;          // pinned, 2 x max_num_pages
   hipEvent_t copied[2] = {nullptr, nullptr};
   bool copy_pending[2] = {false, false};
@@ -187,8 +194,11 @@ SPKV_API int spkv_create(const spkv_config* cfg, void* const* pool_ptrs,
   h->ws_bytes = workspace_bytes;
   h->dev_table[0] = reinterpret_cast<int32_t*>(h->ws);
   h->dev_table[1] = reinterpret_cast<int32_t*>(h->ws + sz.table_bytes);
-  h->partials = h->ws + 2 * sz.table_bytes;
-  const int64_t room = workspace_bytes - 2 * sz.table_bytes;
+  h->dev_rowmap[0] = reinterpret_cast<uint32_t*>(h->ws + 2 * sz.table_bytes);
+  h->dev_rowmap[1] = reinterpret_cast<uint32_t*>(h->ws + 2 * sz.table_bytes +
+                                                 sz.rowmap_bytes);
+  h->partials = h->ws + sz.min_ws;
+  const int64_t room = workspace_bytes - sz.min_ws;
   h->max_splits = static_cast<int>(
       std::max<int64_t>(1, std::min<int64_t>(kMaxSplits, room / sz.per_split)));
   if (hipHostMalloc(reinterpret_cast<void**>(&h->stage),
@@ -311,9 +321,23 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream) {
   int32_t* host = h->stage + size_t(slot) * h->g.max_num_pages;
   std::memcpy(host, pv.table, size_t(pv.n_pages) * sizeof(int32_t));
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const spkv::Geometry& g = h->g;
+  spkv::PlanArgs pa;
+  pa.table = h->dev_table[slot];
+  pa.rowmap = h->dev_rowmap[slot];
+  pa.n_patch = pv.n_patch;
+  pa.n_pages = pv.n_pages;
+  pa.patch_len = g.patch_tokens;
+  pa.special_len = g.num_special * g.frames_per_spage;
+  pa.last_len = pv.last_page_len;
+  pa.page_size = g.page_size;
+  pa.nk = static_cast<int32_t>(pv.visible_tokens);
+  pa.n_out = static_cast<int32_t>(
+      round_up(pv.visible_tokens, spkv::kAttnKeyTile) + spkv::kRowmapPad);
   if (hipMemcpyAsync(h->dev_table[slot], host, size_t(pv.n_pages) * sizeof(int32_t),
                      hipMemcpyHostToDevice, st) != hipSuccess ||
-      hipEventRecord(h->copied[slot], st) != hipSuccess) {
+      hipEventRecord(h->copied[slot], st) != hipSuccess ||
+      spkv::launch_expand(pa, st) != hipSuccess) {
     return SPKV_ERR_HIP;  // the pending plan is simply not committed
   }
   h->pool->commit_plan();
@@ -372,7 +396,7 @@ SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
   DeviceGuard guard(h->device);
   spkv::AttnArgs a;
   a.pool = static_cast<const uint16_t*>(h->pools[block]);
-  a.table = h->dev_table[h->plan_slot];
+  a.rowmap = h->dev_rowmap[h->plan_slot];
   a.q = static_cast<const uint16_t*>(q);
   a.out = static_cast<uint16_t*>(out);
   const int64_t rows = int64_t(nq) * g.num_heads;
@@ -382,11 +406,6 @@ SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
   a.nq = nq;
   a.num_heads = g.num_heads;
   a.page_size = g.page_size;
-  a.patch_len = g.patch_tokens;
-  a.special_len = g.num_special * g.frames_per_spage;
-  a.n_patch = pv.n_patch;
-  a.n_pages = pv.n_pages;
-  a.last_len = pv.last_page_len;
   a.nk = static_cast<int32_t>(nk);
   a.splits = static_cast<int32_t>(splits);
   a.tokens_per_split = static_cast<int32_t>(tiles_per_split * spkv::kAttnKeyTile);

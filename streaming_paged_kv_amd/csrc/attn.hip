@@ -1,4 +1,5 @@
-// run(): paged prefill attention over the planned page table (gfx950).
+// plan()'s device half and run(): paged prefill attention over the planned
+// pages (gfx950).
 //
 // What it computes ("How LingBot-Map Implements the KV Cache Mechanism ...",
 // section "Kernel-Level Execution Flow"): for every query row i and head h of
@@ -12,6 +13,11 @@
 // special page's fill is described by last_page_len, so no mask is needed).
 //
 // Design (gfx950 / CDNA4):
+//  * plan() expands the page table once per frame step into a row map (pool
+//    row of every visible token) with a small kernel, so the attention loop
+//    never divides or looks up pages: pages of any length (999, 996-token
+//    special pages, a partly filled last page) are walked as one token
+//    sequence, without padding.
 //  * One workgroup = 4 waves = 256 query rows of one head; each wave owns 64
 //    rows as two 32-row column tiles of v_mfma_f32_32x32x16_bf16.
 //  * Scores are computed transposed, S^T = K Q^T: a lane then holds one query
@@ -21,12 +27,13 @@
 //    P never leaves registers; the key order inside each 16-key step is the
 //    MFMA output order, and V^T is stored in LDS in that order.
 //  * Online softmax in fp32, in base 2 with s*log2(e) folded into one FMA;
-//    P is rounded to bf16 for the second product; O is rounded to bf16 once.
-//  * K/V tiles of 64 tokens are walked across page boundaries in table order,
-//    so pages of any length (999, 996-token special pages, a partly filled
-//    last page) are consumed without padding; only the last tile of a key
-//    range is masked.  Tiles are double-buffered in LDS and the next tile's
-//    global loads are in flight while the current one is computed.
+//    the running maximum is only raised (and O, l rescaled) when a tile's
+//    maximum exceeds it by more than 2^8, a wave-uniform decision, so most
+//    tiles skip the rescale.  P is rounded to bf16 for the second product; O
+//    is rounded to bf16 once.
+//  * K/V tiles of 64 tokens are double-buffered in LDS; the next tile's K/V
+//    loads and the row ids of the tile after it are in flight while the
+//    current tile is computed.
 //  * The key range is split across workgroups when the query tiles x heads
 //    alone cannot fill 256 CUs; partial (O, m, l) go to the workspace and a
 //    merge kernel combines them.  Work items are mapped so that the query
@@ -48,40 +55,30 @@ constexpr int kBM = kAttnQueryTile;    // query rows per workgroup
 constexpr int kRow = 72;               // LDS row pitch in bf16 (144 B)
 constexpr int kTile = kBN * kRow;      // one K or V^T tile in LDS
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;  // log2 headroom before rescaling
 
-// Valid tokens of table entry e.
-__device__ __forceinline__ int entry_len(const AttnArgs& a, int e) {
-  return e < a.n_patch ? a.patch_len
-                       : (e < a.n_pages - 1 ? a.special_len : a.last_len);
-}
-
-// Position (table entry, offset) of visible token t, t < nk.
-__device__ __forceinline__ void locate(const AttnArgs& a, int t, int& e,
-                                       int& o) {
-  const int patch_tokens = a.n_patch * a.patch_len;
-  if (t < patch_tokens) {
-    e = t / a.patch_len;
-    o = t - e * a.patch_len;
+// ------------------------------------------------------------- plan expand
+__global__ __launch_bounds__(256) void expand_kernel(PlanArgs p) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= p.n_out) return;
+  const int tt = min(t, p.nk - 1);
+  const int patch_tokens = p.n_patch * p.patch_len;
+  int e, o;
+  if (tt < patch_tokens) {
+    e = tt / p.patch_len;
+    o = tt - e * p.patch_len;
   } else {
-    const int u = t - patch_tokens;
-    const int k = u / a.special_len;
-    e = a.n_patch + k;
-    o = u - k * a.special_len;
+    const int u = tt - patch_tokens;
+    const int k = u / p.special_len;
+    e = p.n_patch + k;
+    o = u - k * p.special_len;
   }
+  p.rowmap[t] = static_cast<uint32_t>(p.table[e]) * 2u *
+                    static_cast<uint32_t>(p.page_size) +
+                static_cast<uint32_t>(o);
 }
 
-// Move a position n tokens forward (positions past the end get e = n_pages).
-__device__ __forceinline__ void advance(const AttnArgs& a, int& e, int& o,
-                                        int n) {
-  o += n;
-  while (e < a.n_pages) {
-    const int len = entry_len(a, e);
-    if (o < len) break;
-    o -= len;
-    ++e;
-  }
-}
-
+// ---------------------------------------------------------------- attention
 // Swap bits 2 and 3 of a key index: the order in which one 16-key step of
 // the MFMA output holds its keys (see the file comment).
 __device__ __forceinline__ int key_pos(int k) {
@@ -95,30 +92,16 @@ struct TileRegs {
 
 // Each thread fetches 4 consecutive tokens x 4 dims (8 bytes) of K and of V.
 // A wave covers 16 tokens x 128 B per load: full 128-byte rows.
-__device__ __forceinline__ void load_tile(const AttnArgs& a, int h, int c,
-                                          int e, int o, int t, int t_end,
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ pool,
+                                          uint4 rid, size_t col_off,
+                                          size_t hd, size_t v_off,
                                           TileRegs& r) {
-  const size_t hd = size_t(a.num_heads) * kD;
-  const size_t page_elems = size_t(a.page_size) * hd;
+  const uint32_t ids[4] = {rid.x, rid.y, rid.z, rid.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (t + i < t_end && e < a.n_pages) {
-      const size_t page = static_cast<size_t>(a.table[e]);
-      const size_t off = (page * 2) * page_elems + size_t(o) * hd +
-                         size_t(h) * kD + size_t(c) * 4;
-      r.k[i] = *reinterpret_cast<const uint2*>(a.pool + off);
-      r.v[i] = *reinterpret_cast<const uint2*>(a.pool + off + page_elems);
-    } else {
-      r.k[i] = make_uint2(0u, 0u);
-      r.v[i] = make_uint2(0u, 0u);
-    }
-    if (e < a.n_pages) {
-      ++o;
-      if (o >= entry_len(a, e)) {
-        o = 0;
-        ++e;
-      }
-    }
+    const uint16_t* p = pool + size_t(ids[i]) * hd + col_off;
+    r.k[i] = *reinterpret_cast<const uint2*>(p);
+    r.v[i] = *reinterpret_cast<const uint2*>(p + v_off);
   }
 }
 
@@ -134,10 +117,14 @@ __device__ __forceinline__ void store_tile(uint16_t* ks, uint16_t* vt, int q4,
   const uint32_t lo0 = r.v[0].x, lo1 = r.v[1].x, lo2 = r.v[2].x, lo3 = r.v[3].x;
   const uint32_t hi0 = r.v[0].y, hi1 = r.v[1].y, hi2 = r.v[2].y, hi3 = r.v[3].y;
   uint2 col[4];
-  col[0] = make_uint2((lo0 & 0xffffu) | (lo1 << 16), (lo2 & 0xffffu) | (lo3 << 16));
-  col[1] = make_uint2((lo0 >> 16) | (lo1 & 0xffff0000u), (lo2 >> 16) | (lo3 & 0xffff0000u));
-  col[2] = make_uint2((hi0 & 0xffffu) | (hi1 << 16), (hi2 & 0xffffu) | (hi3 << 16));
-  col[3] = make_uint2((hi0 >> 16) | (hi1 & 0xffff0000u), (hi2 >> 16) | (hi3 & 0xffff0000u));
+  col[0] = make_uint2(__builtin_amdgcn_perm(lo1, lo0, 0x05040100u),
+                      __builtin_amdgcn_perm(lo3, lo2, 0x05040100u));
+  col[1] = make_uint2(__builtin_amdgcn_perm(lo1, lo0, 0x07060302u),
+                      __builtin_amdgcn_perm(lo3, lo2, 0x07060302u));
+  col[2] = make_uint2(__builtin_amdgcn_perm(hi1, hi0, 0x05040100u),
+                      __builtin_amdgcn_perm(hi3, hi2, 0x05040100u));
+  col[3] = make_uint2(__builtin_amdgcn_perm(hi1, hi0, 0x07060302u),
+                      __builtin_amdgcn_perm(hi3, hi2, 0x07060302u));
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     *reinterpret_cast<uint2*>(vt + (4 * c + j) * kRow + pos) = col[j];
@@ -149,6 +136,103 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
 
 __device__ __forceinline__ float xor32(float x) {
   return __shfl_xor(x, 32, 64);
+}
+
+// One 64-key tile for the wave's NT active 32-query column tiles.
+template <int NT>
+__device__ __forceinline__ void compute_tile(
+    const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vt,
+    const bf16x8 (&qf)[2][4], f32x16 (&o_acc)[2][2], float (&m_run)[2],
+    float (&l_run)[2], int valid, float c2, int col, int half) {
+  // S^T = K Q^T for the tile's two 32-key m-tiles.
+  bf16x8 kf[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      kf[mt][s] = lds_frag(ks + (32 * mt + col) * kRow + 16 * s + 8 * half);
+  f32x16 sc[NT][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt][s], qf[nt][s], acc,
+                                                      0, 0, 0);
+      sc[nt][mt] = acc;
+    }
+
+  if (valid < kBN) {
+    // Keys past the end of the range: lane holds key
+    // 32*mt + (r/4)*8 + half*4 + r%4 in register r.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * mt + (r >> 2) * 8 + half * 4 + (r & 3);
+          if (key >= valid) sc[nt][mt][r] = -INFINITY;
+        }
+  }
+
+  bf16x8 pf[NT][4];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float mx = sc[nt][0][0];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[nt][mt][r]);
+    mx = fmaxf(mx, xor32(mx));
+    const float m_tile = mx * c2;
+    // Raise the running maximum only when this tile would overflow the
+    // slack; the decision is per wave so the branch is uniform.
+    if (__any(m_tile > m_run[nt] + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run[nt], m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+      m_run[nt] = m_new;
+      l_run[nt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) o_acc[nt][dt] *= alpha;
+    }
+    const float mneg = -m_run[nt];
+    float lsum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[nt][mt][r], c2, mneg));
+        sc[nt][mt][r] = p;
+        lsum += p;
+      }
+    l_run[nt] += lsum;
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const int mt = k2 >> 1, r0 = (k2 & 1) * 8;
+      bf16x8 v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (__bf16)sc[nt][mt][r0 + j];
+      pf[nt][k2] = v;
+    }
+  }
+
+  // O^T += V^T P^T.
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt) {
+    bf16x8 vf[4];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2)
+      vf[k2] = lds_frag(vt + (32 * dt + col) * kRow + 16 * k2 + 8 * half);
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        o_acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            vf[k2], pf[nt][k2], o_acc[nt][dt], 0, 0, 0);
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a,
@@ -179,11 +263,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a,
   // Loader role: tokens 4*q4..4*q4+3 of each tile, dims 4*c..4*c+3.
   const int q4 = tid >> 4;
   const int c = tid & 15;
+  const size_t hd = size_t(a.num_heads) * kD;
+  const size_t col_off = size_t(h) * kD + size_t(c) * 4;
+  const size_t v_off = size_t(a.page_size) * hd;
+  const uint32_t* rm = a.rowmap + t_begin + 4 * q4;
 
   // Queries of this wave; Q^T fragments as MFMA B operands.
   const int q0 = qt * kBM + wave * 64;
   const int n_active = (q0 < a.nq) + (q0 + 32 < a.nq);
-  const size_t hd = size_t(a.num_heads) * kD;
   bf16x8 qf[2][4];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -208,17 +295,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a,
   float l_run[2] = {0.f, 0.f};
   const float c2 = a.sm_scale * kLog2e;
 
-  // Prologue: first tile.
-  int e, o;
-  int t_load = t_begin + 4 * q4;
-  if (t_load < a.nk) {
-    locate(a, t_load, e, o);
-  } else {
-    e = a.n_pages;
-    o = 0;
-  }
+  // Prologue: tile 0 into LDS, row ids of tile 1 in registers.  The row map
+  // is padded past the last token, so these reads stay inside it.
   TileRegs regs;
-  load_tile(a, h, c, e, o, t_load, t_end, regs);
+  uint4 rid = *reinterpret_cast<const uint4*>(rm);
+  load_tile(a.pool, rid, col_off, hd, v_off, regs);
+  rid = *reinterpret_cast<const uint4*>(rm + kBN);
   store_tile(lds, lds + kTile, q4, c, regs);
   __syncthreads();
 
@@ -228,103 +310,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a,
     const uint16_t* vt = ks + kTile;
     const bool more = it + 1 < n_tiles;
     if (more) {
-      advance(a, e, o, kBN);
-      t_load += kBN;
-      load_tile(a, h, c, e, o, t_load, t_end, regs);
+      load_tile(a.pool, rid, col_off, hd, v_off, regs);
+      rid = *reinterpret_cast<const uint4*>(rm + (it + 2) * kBN);
     }
 
-    if (n_active > 0) {
-      const int tile0 = t_begin + it * kBN;
-      const int valid = t_end - tile0;  // < kBN only on the last tile
-
-      // S^T = K Q^T for two 32-key m-tiles.
-      f32x16 sc[2][2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        bf16x8 kf[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          kf[s] = lds_frag(ks + (32 * mt + col) * kRow + 16 * s + 8 * half);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          f32x16 acc = f32x16{};
-          if (nt < n_active) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nt][s],
-                                                            acc, 0, 0, 0);
-          }
-          sc[nt][mt] = acc;
-        }
-      }
-
-      if (valid < kBN) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = 32 * mt + (r >> 2) * 8 + half * 4 + (r & 3);
-              if (key >= valid) sc[nt][mt][r] = -INFINITY;
-            }
-      }
-
-      // Online softmax per query column (base 2).
-      bf16x8 pf[2][4];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        if (nt >= n_active) {
-#pragma unroll
-          for (int ks2 = 0; ks2 < 4; ++ks2) pf[nt][ks2] = bf16x8{};
-          continue;
-        }
-        float mx = sc[nt][0][0];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[nt][mt][r]);
-        mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(m_run[nt], mx * c2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-        m_run[nt] = m_new;
-        float lsum = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p =
-                __builtin_amdgcn_exp2f(fmaf(sc[nt][mt][r], c2, -m_new));
-            sc[nt][mt][r] = p;
-            lsum += p;
-          }
-        l_run[nt] = l_run[nt] * alpha + lsum;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) o_acc[nt][dt] *= alpha;
-#pragma unroll
-        for (int ks2 = 0; ks2 < 4; ++ks2) {
-          const int mt = ks2 >> 1, r0 = (ks2 & 1) * 8;
-          bf16x8 v;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = (__bf16)sc[nt][mt][r0 + j];
-          pf[nt][ks2] = v;
-        }
-      }
-
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-#pragma unroll
-        for (int ks2 = 0; ks2 < 4; ++ks2) {
-          const bf16x8 vf =
-              lds_frag(vt + (32 * dt + col) * kRow + 16 * ks2 + 8 * half);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            if (nt < n_active)
-              o_acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  vf, pf[nt][ks2], o_acc[nt][dt], 0, 0, 0);
-        }
-      }
+    const int valid = t_end - (t_begin + it * kBN);  // < kBN on the last tile
+    if (n_active == 2) {
+      compute_tile<2>(ks, vt, qf, o_acc, m_run, l_run, valid, c2, col, half);
+    } else if (n_active == 1) {
+      compute_tile<1>(ks, vt, qf, o_acc, m_run, l_run, valid, c2, col, half);
     }
 
     if (more) {
@@ -419,6 +413,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 }
 
 }  // namespace
+
+hipError_t launch_expand(const PlanArgs& p, hipStream_t stream) {
+  hipLaunchKernelGGL(expand_kernel, dim3((p.n_out + 255) / 256), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.nq + kBM - 1) / kBM;

@@ -22,26 +22,43 @@ struct AppendArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
-// One attention run over a planned page table.
-struct AttnArgs {
-  const uint16_t* pool;     // block's pool (bf16 bits)
+// Expansion of a plan's page table into a per-token row map: for visible
+// token t, the pool row (page * 2 * page_size + offset) of its K; its V is
+// page_size rows further.  Entries past the last token repeat the last
+// token's row, so a tile that runs past the end reads valid memory.
+struct PlanArgs {
   const int32_t* table;     // device page table, n_pages entries
-  const uint16_t* q;        // [nq][H][D]
-  uint16_t* out;            // [nq][H][D]
-  float* part_o;            // [splits][nq][H][D]     (splits > 1)
-  float* part_ml;           // [splits][nq][H][2]     (splits > 1)
-  int32_t nq, num_heads, page_size;
+  uint32_t* rowmap;         // out: n_out entries
+  int32_t n_patch, n_pages;
   int32_t patch_len;        // valid tokens of a patch page
   int32_t special_len;      // valid tokens of a full special page
-  int32_t n_patch, n_pages, last_len;
+  int32_t last_len;         // valid tokens of the last special page
+  int32_t page_size;
   int32_t nk;               // visible tokens
-  int32_t splits, tokens_per_split;
-  float sm_scale;
+  int32_t n_out;            // entries written (nk rounded up, plus padding)
 };
 
 // Key tiles the kernel uses; run() sizes the split from it.
 constexpr int kAttnKeyTile = 64;
 constexpr int kAttnQueryTile = 256;
+// Row-map entries written past the visible tokens.
+constexpr int kRowmapPad = 2 * kAttnKeyTile;
+
+hipError_t launch_expand(const PlanArgs& p, hipStream_t stream);
+
+// One attention run over a planned row map.
+struct AttnArgs {
+  const uint16_t* pool;     // block's pool (bf16 bits)
+  const uint32_t* rowmap;   // token -> K row of the pool (see PlanArgs)
+  const uint16_t* q;        // [nq][H][D]
+  uint16_t* out;            // [nq][H][D]
+  float* part_o;            // [splits][nq][H][D]     (splits > 1)
+  float* part_ml;           // [splits][nq][H][2]     (splits > 1)
+  int32_t nq, num_heads, page_size;
+  int32_t nk;               // visible tokens
+  int32_t splits, tokens_per_split;
+  float sm_scale;
+};
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 

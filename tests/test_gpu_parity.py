@@ -292,7 +292,7 @@ def full_size(name, num_blocks=None, attn_blocks=(0, 11, 23), pool_blocks=(0, 23
                 got = outs[b][rows]
                 mx, mean, rel = H.compare(got, ref, (name, f, b))
                 checked += 1
-            log(f"  frame {f} checked (Nk={sum(plans[f][1:2])} pages)")
+            log(f"  frame {f} ({kind}) checked: {len(plans[f][0])} pages visible")
     cache.close()
     assert checked >= len(milestones)
 
