@@ -105,7 +105,6 @@ def cpu_baseline(wl, warm_frames, n_blocks_timed):
     t0 = time.perf_counter()
     one_frame(f, "key", 0)          # the host steps of a frame, all blocks
     t_host = time.perf_counter() - t0
-    o2 = None
     t0 = time.perf_counter()
     pl = o.plan()
     for b in range(n_blocks_timed):
@@ -152,8 +151,10 @@ def main():
     cache = spkv.PagedKVCache(**wl.cfg_kwargs(), device=dev)
     nb = wl.num_blocks
     S, W = wl.scale_frames, wl.sliding_window
-    total = args.warmup + args.steps
-    sched = frame_schedule(wl, total)
+    n_attn = 0 if args.no_events else args.steps     # window B frames
+    n_app = 0 if args.no_events else min(args.steps, 20)  # window C frames
+    total = args.warmup + args.steps + n_attn
+    sched = frame_schedule(wl, total + n_app)
 
     # input bank, resident in HBM before timing
     nbank = max(1, min(args.bank, total))
@@ -165,11 +166,15 @@ def main():
     hd = wl.num_heads * wl.head_dim
     nq = wl.tokens_per_frame
 
-    use_ev = not args.no_events
+    # Three windows over consecutive frames of the same stream:
+    #   A  the timed region (value, ms_per_step): no events at all, since each
+    #      timing event adds a few microseconds of idle time on the stream;
+    #   B  events around every run() only: the attention kernel's duration;
+    #   C  events around every append only: the append kernel's bandwidth.
     ev_attn, ev_app = [], []
     flops, app_bytes = [], []
 
-    def step(f, record):
+    def step(f, mode):
         kind = sched[f]
         qkv = bank[f % nbank]
         if wl.dynamic or kind == "transient":
@@ -177,30 +182,30 @@ def main():
         nk = None
         for b in range(nb):
             q, k, v = qkv[b]
-            if record:
+            if mode == "C":
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
             cache.append_frame(b, k, v, stream=stream)
-            if record:
+            if mode == "C":
                 e1.record(stream)
                 ev_app.append((e0, e1))
                 app_bytes.append(8 * nq * hd)
             cache.evict_frames(b, S, W)
             if b == 0:
                 cache.plan(stream=stream)
-                if record:
+                if mode == "B":
                     tab, npatch, lpl = cache.get_plan()
                     nsp = len(tab) - npatch
                     nk = (npatch * wl.patch_tokens +
                           (nsp - 1) * wl.num_special_tokens *
                           (wl.page_size // wl.num_special_tokens) + lpl)
-            if record:
+            if mode == "B":
                 a0 = torch.cuda.Event(enable_timing=True)
                 a1 = torch.cuda.Event(enable_timing=True)
                 a0.record(stream)
             cache.run(b, q, out=outs[b], sm_scale=sm, stream=stream)
-            if record:
+            if mode == "B":
                 a1.record(stream)
                 ev_attn.append((a0, a1))
                 flops.append(4.0 * nq * nk * hd)
@@ -213,13 +218,20 @@ def main():
             cache.set_defer_eviction(False)
 
     for f in range(args.warmup):
-        step(f, False)
+        step(f, None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for f in range(args.warmup, total):
-        step(f, use_ev)
+    for f in range(args.warmup, args.warmup + args.steps):
+        step(f, None)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    use_ev = not args.no_events
+    if use_ev:
+        for f in range(args.warmup + args.steps, total):
+            step(f, "B")
+        for f in range(total, total + n_app):
+            step(f, "C")
+        torch.cuda.synchronize()
 
     result = {
         "metric": METRIC,
@@ -241,7 +253,7 @@ def main():
                          f"S/W/R={wl.scale_frames}/{wl.sliding_window}/{wl.headroom}, "
                          f"keyframe_interval={wl.keyframe_interval}"
                          + (", dynamic accept/rollback" if wl.dynamic else "")),
-            "frames_timed": f"{args.warmup}..{total - 1}",
+            "frames_timed": f"{args.warmup}..{args.warmup + args.steps - 1}",
             "input_bank_frames": nbank,
         },
     }
@@ -259,6 +271,8 @@ def main():
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": None,
             "kernel": "attn_kernel (+ split merge) per run()",
+            "window": (f"frames {args.warmup + args.steps}..{total - 1}, HIP events "
+                       f"around each run() on its stream"),
             "avg_launch_us": avg_attn * 1e6,
             "algorithmic_flops_per_launch": avg_flops,
         }
@@ -267,6 +281,7 @@ def main():
             "bound": "hbm", "achieved": app_gbs, "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": app_gbs / PEAK_HBM_GBS,
             "avg_launch_us": sum(t_app) / len(t_app) * 1e6,
+            "window": f"frames {total}..{total + n_app - 1}, events around append",
             "bytes_per_launch": app_bytes[0],
         }
     cache.close()

@@ -29,8 +29,9 @@
 //  * Online softmax in fp32, in base 2 with s*log2(e) folded into one FMA;
 //    the running maximum is only raised (and O, l rescaled) when a tile's
 //    maximum exceeds it by more than 2^8, a wave-uniform decision, so most
-//    tiles skip the rescale.  P is rounded to bf16 for the second product; O
-//    is rounded to bf16 once.
+//    tiles skip the rescale.  P is rounded to bf16 for the second product and
+//    the row sums are taken from the same rounded values with
+//    v_dot2_f32_bf16 (two per instruction); O is rounded to bf16 once.
 //  * K/V tiles of 64 tokens are double-buffered in LDS; the next tile's K/V
 //    loads and the row ids of the tile after it are in flight while the
 //    current tile is computed.
@@ -46,6 +47,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 64;
 constexpr int kBN = kAttnKeyTile;      // keys per tile
@@ -91,17 +93,18 @@ struct TileRegs {
 };
 
 // Each thread fetches 4 consecutive tokens x 4 dims (8 bytes) of K and of V.
-// A wave covers 16 tokens x 128 B per load: full 128-byte rows.
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ pool,
-                                          uint4 rid, size_t col_off,
-                                          size_t hd, size_t v_off,
-                                          TileRegs& r) {
+// A wave covers 16 tokens x 128 B per load: full 128-byte rows.  Offsets are
+// 32-bit byte offsets from uniform bases (a block's pool is below 4 GiB).
+__device__ __forceinline__ void load_tile(const char* __restrict__ kbase,
+                                          const char* __restrict__ vbase,
+                                          uint4 rid, uint32_t row_bytes,
+                                          uint32_t col_bytes, TileRegs& r) {
   const uint32_t ids[4] = {rid.x, rid.y, rid.z, rid.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint16_t* p = pool + size_t(ids[i]) * hd + col_off;
-    r.k[i] = *reinterpret_cast<const uint2*>(p);
-    r.v[i] = *reinterpret_cast<const uint2*>(p + v_off);
+    const uint32_t off = ids[i] * row_bytes + col_bytes;
+    r.k[i] = *reinterpret_cast<const uint2*>(kbase + off);
+    r.v[i] = *reinterpret_cast<const uint2*>(vbase + off);
   }
 }
 
@@ -198,25 +201,27 @@ __device__ __forceinline__ void compute_tile(
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) o_acc[nt][dt] *= alpha;
     }
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     const float mneg = -m_run[nt];
     float lsum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[nt][mt][r], c2, mneg));
-        sc[nt][mt][r] = p;
-        lsum += p;
-      }
-    l_run[nt] += lsum;
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
       const int mt = k2 >> 1, r0 = (k2 & 1) * 8;
       bf16x8 v;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = (__bf16)sc[nt][mt][r0 + j];
+      for (int j = 0; j < 8; j += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[nt][mt][r0 + j], c2, mneg));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[nt][mt][r0 + j + 1], c2, mneg));
+        bf16x2 pk;
+        pk[0] = (__bf16)p0;
+        pk[1] = (__bf16)p1;
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lsum, false);
+        v[j] = pk[0];
+        v[j + 1] = pk[1];
+      }
       pf[nt][k2] = v;
     }
+    l_run[nt] += lsum;
   }
 
   // O^T += V^T P^T.
@@ -264,8 +269,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a,
   const int q4 = tid >> 4;
   const int c = tid & 15;
   const size_t hd = size_t(a.num_heads) * kD;
-  const size_t col_off = size_t(h) * kD + size_t(c) * 4;
-  const size_t v_off = size_t(a.page_size) * hd;
+  const uint32_t row_bytes = uint32_t(hd) * 2u;
+  const uint32_t col_bytes = uint32_t(c) * 8u;
+  const char* kbase = reinterpret_cast<const char*>(a.pool) + size_t(h) * kD * 2;
+  const char* vbase = kbase + size_t(a.page_size) * row_bytes;
   const uint32_t* rm = a.rowmap + t_begin + 4 * q4;
 
   // Queries of this wave; Q^T fragments as MFMA B operands.
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a,
   // is padded past the last token, so these reads stay inside it.
   TileRegs regs;
   uint4 rid = *reinterpret_cast<const uint4*>(rm);
-  load_tile(a.pool, rid, col_off, hd, v_off, regs);
+  load_tile(kbase, vbase, rid, row_bytes, col_bytes, regs);
   rid = *reinterpret_cast<const uint4*>(rm + kBN);
   store_tile(lds, lds + kTile, q4, c, regs);
   __syncthreads();
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a,
     const uint16_t* vt = ks + kTile;
     const bool more = it + 1 < n_tiles;
     if (more) {
-      load_tile(a.pool, rid, col_off, hd, v_off, regs);
+      load_tile(kbase, vbase, rid, row_bytes, col_bytes, regs);
       rid = *reinterpret_cast<const uint4*>(rm + (it + 2) * kBN);
     }
 
