@@ -25,6 +25,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "streamed frames/s (24-block paged attn, 999-token pages); % bf16 MFMA peak"
+ATTN_SRC = os.path.join(ROOT, "streaming_paged_kv_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel-518x378-traffic.txt")
+COPY_BYTES = 256 << 20        # plain copy used to calibrate the byte counters
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
@@ -131,6 +134,30 @@ def cpu_baseline(wl, warm_frames, n_blocks_timed):
                    f"({t_attn:.2f} s per block), scaled to {wl.num_blocks} blocks; "
                    f"host cores {cores}, BLAS threads {blas}"),
     }
+
+
+def kernel_hash():
+    import hashlib
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary, if
+    it was taken on the current kernel source and this workload."""
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith(("#", "|")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256_16") != kernel_hash():
+            return None
+        if kv.get("workload") != workload:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -269,7 +296,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": recorded_traffic(wl.name),
             "kernel": "attn_kernel (+ split merge) per run()",
             "window": (f"frames {args.warmup + args.steps}..{total - 1}, HIP events "
                        f"around each run() on its stream"),
@@ -286,6 +313,13 @@ def main():
         }
     cache.close()
     del bank
+    # Plain copy of known size, outside every window: the factor between its
+    # byte counters and COPY_BYTES calibrates the attention kernel's.
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.warmup, args.cpu_blocks)

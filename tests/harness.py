@@ -5,10 +5,8 @@ compared at chosen frames.  The two sides share only the inputs (synth)."""
 import numpy as np
 import torch
 
-import streaming_paged_kv_amd as spkv
 import synth
-from oracle import OracleConfig, PagePoolOracle, bf16_bits_to_f64
-from oracle.attention import paged_attention
+from oracle import OracleConfig, PagePoolOracle
 
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
@@ -33,35 +31,7 @@ def frame_kinds(wl, frames=None):
     return out
 
 
-def oracle_step(o, wl, f, kind, reset, kv_of_block, on_plan=None):
-    """One frame on the oracle side (all blocks).  kv_of_block(b) -> (k, v)
-    uint16 bits or (None, None) for untracked blocks."""
-    S, W = wl.scale_frames, wl.sliding_window
-    if reset:
-        o.reset()
-    if wl.dynamic:
-        o.set_defer_eviction(True)
-    if kind == "transient":
-        o.set_defer_eviction(True)
-    for b in range(wl.num_blocks):
-        k, v = kv_of_block(b)
-        o.append_frame(b, k, v)
-        o.evict_frames(b, S, W)
-        if b == 0:
-            o.plan()
-            if on_plan is not None:
-                on_plan(o)
-        o.check_run(b)
-    for b in range(wl.num_blocks):
-        if kind in ("transient", "reject"):
-            o.rollback_last_frame(b)
-        elif kind == "accept":
-            o.execute_deferred_eviction(b, S, W)
-    if kind == "transient":
-        o.set_defer_eviction(False)
-
-
-def gpu_step(cache, wl, kind, reset, qkv, outs, blocks_out=None, stream=None):
+def gpu_step(cache, wl, kind, reset, qkv, outs, stream=None):
     """One frame on the HIP side.  qkv[b] = (q, k, v) device tensors; the
     run's output for block b is written into outs[b]."""
     S, W = wl.scale_frames, wl.sliding_window
@@ -172,10 +142,6 @@ def compare(gpu_bf16, ref_f64, what):
     assert mean_abs <= MEAN_ABS, (what, mean_abs)
     assert rel <= REL_L2, (what, rel)
     return max_abs, mean_abs, rel
-
-
-def pool_bits(t):
-    return synth.bf16_bits(t)
 
 
 def gen_frame(wl, f, nblocks, device):

@@ -12,8 +12,8 @@ import torch
 
 import synth
 import harness as H
-from oracle import OracleConfig, PagePoolOracle, bf16_bits_to_f64
-from oracle.attention import paged_attention, dense_attention
+from oracle import OracleConfig, PagePoolOracle
+from oracle.attention import paged_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -53,10 +53,6 @@ def full_parity(wl, frames=None, splits=0):
         outs = [torch.empty_like(x[0]) for x in qkv]
         # oracle first so that its attention uses the state of this frame
         ref = {}
-
-        def on_plan(oo):
-            pass
-
         S, W = wl.scale_frames, wl.sliding_window
         if reset:
             o.reset()
@@ -156,7 +152,6 @@ def test_edge_cases_nq_scale_and_sharp_keys():
     cfg = OracleConfig(**wl.cfg_kwargs())
     o = PagePoolOracle(cfg, track_pool=[0])
     cache = new_cache(wl)
-    gen = torch.Generator(device="cpu").manual_seed(5)
     for f in range(wl.frames):
         q, k, v = synth.frame_qkv(wl, f, 0, device=DEV)
         if f == 3:
@@ -176,7 +171,6 @@ def test_edge_cases_nq_scale_and_sharp_keys():
             torch.cuda.synchronize()
             ref = paged_attention(o.pools[0], pl, cfg, qb[:nq], sm)
             H.compare(out, ref, ("edge", f, nq, sm))
-    # constant V over all visible tokens gives that constant
     cache.close()
 
 
@@ -222,6 +216,7 @@ def full_size(name, num_blocks=None, attn_blocks=(0, 11, 23), pool_blocks=(0, 23
     sm = wl.head_dim ** -0.5
     ns = wl.num_special_tokens
     rows = H.sample_rows(wl.tokens_per_frame)
+    assert len(rows) > 20
     outs = [torch.empty((wl.tokens_per_frame, wl.num_heads, wl.head_dim),
                         dtype=torch.bfloat16, device=DEV) for _ in range(nb)]
     checked = 0
@@ -242,10 +237,6 @@ def full_size(name, num_blocks=None, attn_blocks=(0, 11, 23), pool_blocks=(0, 23
 
         refs = {}
         snap = {}
-
-        def on_plan(oo, f=f):
-            pass
-
         # oracle side, capturing the attention references before rollback
         S, W = wl.scale_frames, wl.sliding_window
         if reset:
