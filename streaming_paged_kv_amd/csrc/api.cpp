@@ -382,8 +382,8 @@ SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
   if (h->forced_splits > 0) {
     splits = h->forced_splits;
   } else {
-    // Two resident workgroups per CU; each split keeps >= 4 key tiles.
-    const int64_t want = 2 * int64_t(h->num_cus);
+    // One resident workgroup per CU; each split keeps >= 4 key tiles.
+    const int64_t want = int64_t(h->num_cus);
     const int64_t units = n_qtiles * g.num_heads;
     splits = (want + units - 1) / units;
     splits = std::min<int64_t>(splits, std::max<int64_t>(1, n_ktiles / 4));

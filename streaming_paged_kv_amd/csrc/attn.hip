@@ -18,25 +18,35 @@
 //    never divides or looks up pages: pages of any length (999, 996-token
 //    special pages, a partly filled last page) are walked as one token
 //    sequence, without padding.
-//  * One workgroup = 4 waves = 256 query rows of one head; each wave owns 64
+//  * One workgroup = 8 waves = 512 query rows of one head; each wave owns 64
 //    rows as two 32-row column tiles of v_mfma_f32_32x32x16_bf16.
 //  * Scores are computed transposed, S^T = K Q^T: a lane then holds one query
-//    column and 16 keys per 32x32 tile, so the softmax row max and row sum are
-//    in-lane reductions plus one exchange with lane ^ 32.  The same lane
-//    layout is exactly the B operand of the second product O^T = V^T P^T, so
-//    P never leaves registers; the key order inside each 16-key step is the
-//    MFMA output order, and V^T is stored in LDS in that order.
-//  * Online softmax in fp32, in base 2 with s*log2(e) folded into one FMA;
-//    the running maximum is only raised (and O, l rescaled) when a tile's
-//    maximum exceeds it by more than 2^8, a wave-uniform decision, so most
-//    tiles skip the rescale.  P is rounded to bf16 for the second product and
-//    the row sums are taken from the same rounded values with
-//    v_dot2_f32_bf16 (two per instruction); O is rounded to bf16 once.
-//  * K/V tiles of 64 tokens are double-buffered in LDS; the next tile's K/V
-//    loads and the row ids of the tile after it are in flight while the
-//    current tile is computed.
-//  * The key range is split across workgroups when the query tiles x heads
-//    alone cannot fill 256 CUs; partial (O, m, l) go to the workspace and a
+//    column and 16 keys per 32x32 tile, so the softmax reductions are
+//    in-lane plus one exchange with lane ^ 32.  The same lane layout is the B
+//    operand of the second product O^T = V^T P^T, so P never leaves
+//    registers.  V^T fragments are read from the natural [key][d] V tile
+//    with the transposing LDS read (ds_read_b64_tr_b16).
+//  * Ping-pong: waves w and w+4 share a SIMD.  The two groups of four waves
+//    alternate between an MFMA phase (PV of the previous tile, scores of the
+//    current one) and a softmax phase (VALU), one workgroup barrier per
+//    phase, so each SIMD's matrix core and vector ALU work at the same time.
+//  * K/V tiles of 64 tokens come in with direct-to-LDS loads
+//    (global_load_lds_dwordx4) into a 4-stage ring, issued three phases
+//    before their first use; they cost no registers and the wave never
+//    waits for them inside a phase.  LDS rows are 128 B, unpadded, with the
+//    16-byte chunks of row r at slot chunk ^ swz(r & 7): the permutation is
+//    applied on the global side (each lane picks which chunk it fetches), so
+//    both the K reads and the transposing V reads are free of bank
+//    conflicts.  The split's row map is staged in LDS as byte offsets.
+//  * Online softmax in fp32, base 2, with s*log2(e) and the running
+//    reference m folded into one FMA per score.  The reference only moves on
+//    a wave-uniform slow path (first tile, or a tile whose p would exceed
+//    2^16), so most tiles neither take a maximum nor rescale.  Row sums are
+//    fp32 sums of the p values; P is rounded to bf16 for the second product;
+//    O is rounded to bf16 once.  (v_dot2 sums of the rounded values would
+//    share the matrix pipe and stall behind the other wave's MFMAs.)
+//  * The key range is split across workgroups when query tiles x heads
+//    alone cannot fill the CUs; partial (O, m, l) go to the workspace and a
 //    merge kernel combines them.  Work items are mapped so that the query
 //    tiles sharing one (head, key split) land on the same XCD (workgroups are
 //    dealt to the 8 XCDs round-robin), where they share that XCD's L2.
@@ -47,17 +57,22 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 constexpr int kD = 64;
-constexpr int kBN = kAttnKeyTile;      // keys per tile
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBM = kAttnQueryTile;    // query rows per workgroup
-constexpr int kRow = 72;               // LDS row pitch in bf16 (144 B)
-constexpr int kTile = kBN * kRow;      // one K or V^T tile in LDS
+constexpr int kBN = kAttnKeyTile;       // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;   // 512
+constexpr int kBM = kAttnQueryTile;     // query rows per workgroup (8 x 64)
+static_assert(kBM == kWaves * 64, "one 64-row slice per wave");
+constexpr int kRowB = 128;              // LDS bytes of one key row (64 bf16)
+constexpr int kTileB = kBN * kRowB;     // one K or V tile: 8 KiB
+constexpr int kStageB = 2 * kTileB;     // K tile, then V tile
+constexpr int kStages = 4;
+constexpr int kRmMax = kAttnRowmapChunk;  // row-map entries staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.0f;  // log2 headroom before rescaling
+constexpr float kSumLimit = 65536.0f;   // bound on a lane's partial row sum
 
 // ------------------------------------------------------------- plan expand
 __global__ __launch_bounds__(256) void expand_kernel(PlanArgs p) {
@@ -81,95 +96,174 @@ __global__ __launch_bounds__(256) void expand_kernel(PlanArgs p) {
 }
 
 // ---------------------------------------------------------------- attention
-// Swap bits 2 and 3 of a key index: the order in which one 16-key step of
-// the MFMA output holds its keys (see the file comment).
-__device__ __forceinline__ int key_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// LDS slot permutation of the eight 16-byte chunks of a key row r: chunk c
+// sits at slot c ^ swz(r & 7).  For eight consecutive rows a chunk lands on
+// eight distinct slots (K fragment reads, 8 lanes x 16 B per LDS cycle), and
+// for keys 4a..4a+3 the chunk pair {2b, 2b+1} lands on four disjoint slot
+// pairs (transposing V reads, 16 lanes x 8 B).
+__device__ __forceinline__ int swz(int x) { return ((x & 3) << 1) | ((x >> 2) & 1); }
+
+// 16 bytes per lane from base + voff into LDS at lds_addr + 16 * lane.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr)
+               : "memory");
 }
 
-struct TileRegs {
-  uint2 k[4];
-  uint2 v[4];
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+// The direct-to-LDS loads are not known to the compiler, so their waits are
+// explicit; loads complete in order, so the count is exact.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Transposing LDS read: within each 16-lane group, lane j receives element
+// j % 4 of the 8-byte chunks addressed by lanes 4i + j/4, i = 0..3.
+__device__ __forceinline__ v4i16 lds_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(
+          (__attribute__((address_space(3))) char*)(char*)p));
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const char*)(const char*)p));
+}
+
+// Per-lane LDS byte offsets of the MFMA operands inside a tile.
+struct Frag {
+  uint32_t kofs[4];   // K: key row col (+32 per m-tile), dims 16s + 8*half..+7
+  uint32_t vofs[2];   // V: rows 4g + j/4 (+16 per k-step, +8), dims 32dt + ...
 };
 
-// Each thread fetches 4 consecutive tokens x 4 dims (8 bytes) of K and of V.
-// A wave covers 16 tokens x 128 B per load: full 128-byte rows.  Offsets are
-// 32-bit byte offsets from uniform bases (a block's pool is below 4 GiB).
-__device__ __forceinline__ void load_tile(const char* __restrict__ kbase,
-                                          const char* __restrict__ vbase,
-                                          uint4 rid, uint32_t row_bytes,
-                                          uint32_t col_bytes, TileRegs& r) {
-  const uint32_t ids[4] = {rid.x, rid.y, rid.z, rid.w};
+// A wave's share of every tile's loads: waves 0-3 fetch K, waves 4-7 V;
+// wave w&3 fetches keys 16*(w&3) .. +15 in two loads of 8 keys x 128 B.
+struct Dma {
+  const char* base;   // pool + head slice (+ page_size rows for V), uniform
+  uint32_t dst;       // wave's destination inside a stage, uniform
+  uint32_t rm_off;    // lane's key inside a tile
+  uint32_t coff;      // lane's source chunk (bytes), chosen by the swizzle
+};
+
+// Loads of one tile into a stage.  The staged row map holds byte offsets of
+// pool rows (multiples of 128), so the chunk offset is or-ed in.
+__device__ __forceinline__ void issue_tile(const Dma& d, const uint32_t* rm_lds,
+                                           uint32_t stage_addr, int tile) {
+  const uint32_t o0 = rm_lds[tile * kBN + d.rm_off] | d.coff;
+  const uint32_t o1 = rm_lds[tile * kBN + d.rm_off + 8] | d.coff;
+  dma16(d.base, o0, stage_addr + d.dst);
+  dma16(d.base, o1, stage_addr + d.dst + 1024u);
+}
+
+// MFMA phase: O^T += V^T P^T for the previous tile, then S^T = K Q^T for
+// the current one.  All V fragments are requested up front and the K
+// fragments after the first half of the PV products, so the wave waits for
+// LDS once per phase.
+template <int NT, bool PV, bool SC>
+__device__ __forceinline__ void mfma_phase(const char* vtile, const char* ktile,
+                                           const Frag& f, const bf16x8 (&qf)[2][4],
+                                           const bf16x8 (&pf)[2][4],
+                                           f32x16 (&o_acc)[2][2], f32x16 (&sc)[2][2]) {
+  bf16x8 vf[2][4];
+  bf16x8 kf[2][4];
+  if (PV) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t off = ids[i] * row_bytes + col_bytes;
-    r.k[i] = *reinterpret_cast<const uint2*>(kbase + off);
-    r.v[i] = *reinterpret_cast<const uint2*>(vbase + off);
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const char* p = vtile + f.vofs[dt] + 16 * k2 * kRowB;
+        const v4i16 lo = lds_tr(p);
+        const v4i16 hi = lds_tr(p + 8 * kRowB);
+        vf[dt][k2] = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+  } else if (SC) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        kf[mt][s] = *reinterpret_cast<const bf16x8*>(ktile + f.kofs[s] + 32 * mt * kRowB);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (PV) {
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        o_acc[nt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0][k2], pf[nt][k2],
+                                                               o_acc[nt][0], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (SC) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          kf[mt][s] = *reinterpret_cast<const bf16x8*>(ktile + f.kofs[s] + 32 * mt * kRowB);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        o_acc[nt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1][k2], pf[nt][k2],
+                                                               o_acc[nt][1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (SC) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt][s], qf[nt][s], acc, 0, 0, 0);
+        sc[nt][mt] = acc;
+      }
   }
 }
 
-// K rows as they are; V transposed to V^T[d][key_pos(key)] so that one lane's
-// 8 keys of an MFMA step are one 16-byte LDS read.
-__device__ __forceinline__ void store_tile(uint16_t* ks, uint16_t* vt, int q4,
-                                           int c, const TileRegs& r) {
+// p = 2^(s*c - m) of one column tile into bf16 B-operand order (keys
+// 8*(lane/32)+j of each 16-key step); returns the lane's partial row sum.
+__device__ __forceinline__ float exp_pack(const f32x16 (&x)[2], float c, float mneg,
+                                          bf16x8 (&pf)[4]) {
+  float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint2*>(ks + (4 * q4 + i) * kRow + 4 * c) = r.k[i];
-  // 4x4 transpose of 16-bit values: column j of the 4 rows.
-  const int pos = key_pos(4 * q4);
-  const uint32_t lo0 = r.v[0].x, lo1 = r.v[1].x, lo2 = r.v[2].x, lo3 = r.v[3].x;
-  const uint32_t hi0 = r.v[0].y, hi1 = r.v[1].y, hi2 = r.v[2].y, hi3 = r.v[3].y;
-  uint2 col[4];
-  col[0] = make_uint2(__builtin_amdgcn_perm(lo1, lo0, 0x05040100u),
-                      __builtin_amdgcn_perm(lo3, lo2, 0x05040100u));
-  col[1] = make_uint2(__builtin_amdgcn_perm(lo1, lo0, 0x07060302u),
-                      __builtin_amdgcn_perm(lo3, lo2, 0x07060302u));
-  col[2] = make_uint2(__builtin_amdgcn_perm(hi1, hi0, 0x05040100u),
-                      __builtin_amdgcn_perm(hi3, hi2, 0x05040100u));
-  col[3] = make_uint2(__builtin_amdgcn_perm(hi1, hi0, 0x07060302u),
-                      __builtin_amdgcn_perm(hi3, hi2, 0x07060302u));
+  for (int k2 = 0; k2 < 4; ++k2) {
+    const int mt = k2 >> 1, r0 = (k2 & 1) * 8;
+    bf16x8 v;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    *reinterpret_cast<uint2*>(vt + (4 * c + j) * kRow + pos) = col[j];
-}
-
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
-}
-
-// One 64-key tile for the wave's NT active 32-query column tiles.
-template <int NT>
-__device__ __forceinline__ void compute_tile(
-    const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vt,
-    const bf16x8 (&qf)[2][4], f32x16 (&o_acc)[2][2], float (&m_run)[2],
-    float (&l_run)[2], int valid, float c2, int col, int half) {
-  // S^T = K Q^T for the tile's two 32-key m-tiles.
-  bf16x8 kf[2][4];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      kf[mt][s] = lds_frag(ks + (32 * mt + col) * kRow + 16 * s + 8 * half);
-  f32x16 sc[NT][2];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt][s], qf[nt][s], acc,
-                                                      0, 0, 0);
-      sc[nt][mt] = acc;
+    for (int jj = 0; jj < 8; jj += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(x[mt][r0 + jj], c, mneg));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(x[mt][r0 + jj + 1], c, mneg));
+      s0 += p0;
+      s1 += p1;
+      v[jj] = (__bf16)p0;
+      v[jj + 1] = (__bf16)p1;
     }
+    pf[k2] = v;
+  }
+  return s0 + s1;
+}
 
+// Softmax phase for one tile (c = sm_scale * log2 e, m the column's running
+// reference).  Fast path: p = 2^(s*c - m) without taking the tile maximum.
+// While every p stays <= 2^16 the reference may lag the true maximum, and a
+// lane's partial row sum bounds its p, so a sum above the bound (or inf /
+// NaN, as on a column's first tile, where m is -inf) sends that column tile
+// down the slow path: take the tile maximum, move the reference there,
+// rescale O and l, redo p.
+template <int NT>
+__device__ __forceinline__ void softmax_tile(f32x16 (&sc)[2][2], int half, int valid,
+                                             float c, f32x16 (&o_acc)[2][2],
+                                             float (&m_run)[2], float (&l_run)[2],
+                                             bf16x8 (&pf)[2][4]) {
   if (valid < kBN) {
-    // Keys past the end of the range: lane holds key
-    // 32*mt + (r/4)*8 + half*4 + r%4 in register r.
+    // Keys past the end of the range: register r of m-tile mt holds key
+    // 32*mt + (r/4)*8 + 4*half + r%4.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -180,71 +274,153 @@ __device__ __forceinline__ void compute_tile(
           if (key >= valid) sc[nt][mt][r] = -INFINITY;
         }
   }
-
-  bf16x8 pf[NT][4];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float mx = sc[nt][0][0];
+    float lsum = exp_pack(sc[nt], c, -m_run[nt], pf[nt]);
+    if (__any(!(lsum <= kSumLimit))) {
+      float mx = sc[nt][0][0];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[nt][mt][r]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_tile = mx * c2;
-    // Raise the running maximum only when this tile would overflow the
-    // slack; the decision is per wave so the branch is uniform.
-    if (__any(m_tile > m_run[nt] + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run[nt], m_tile);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[nt][mt][r]);
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run[nt], mx * c);
       const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
       m_run[nt] = m_new;
       l_run[nt] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) o_acc[nt][dt] *= alpha;
-    }
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    const float mneg = -m_run[nt];
-    float lsum = 0.f;
-#pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) {
-      const int mt = k2 >> 1, r0 = (k2 & 1) * 8;
-      bf16x8 v;
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[nt][mt][r0 + j], c2, mneg));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[nt][mt][r0 + j + 1], c2, mneg));
-        bf16x2 pk;
-        pk[0] = (__bf16)p0;
-        pk[1] = (__bf16)p1;
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lsum, false);
-        v[j] = pk[0];
-        v[j + 1] = pk[1];
-      }
-      pf[nt][k2] = v;
+      o_acc[nt][0] *= alpha;
+      o_acc[nt][1] *= alpha;
+      lsum = exp_pack(sc[nt], c, -m_new, pf[nt]);
     }
     l_run[nt] += lsum;
   }
+}
 
-  // O^T += V^T P^T.
+// The phases of one wave over the T tiles of a chunk whose row map is staged
+// in LDS and whose tiles 0..S-3 are in flight.  Iteration k covers phases 2k and 2k+1, each ended by
+// a workgroup barrier.  Group 0 (waves 0-3): [MFMA: PV of tile k-1, scores
+// of tile k][softmax of tile k]; group 1 one phase later: [softmax of tile
+// k-1][MFMA: PV of tile k-1, scores of tile k].  Tile k occupies its stage
+// from phase 2k to 2k+3.  At phase 2k every wave issues its share of tile
+// k+S-2 into the stage that tile k-2 left, and before the barrier that ends
+// phase 2k+1 it waits for its share of tile k+1.  The first and last
+// iterations are peeled so that the loop body has one MFMA shape.
+template <int NT, int GROUP>
+__device__ __forceinline__ void chunk_phases(
+    const Dma& d, const uint32_t* rm_lds, const char* lds, uint32_t lds_addr, int T,
+    int last_valid, const Frag& f, int half, float c, const bf16x8 (&qf)[2][4],
+    f32x16 (&o_acc)[2][2], float (&m_run)[2], float (&l_run)[2]) {
+  f32x16 sc[2][2];
+  bf16x8 pf[2][4];
+  auto kt = [&](int k) { return lds + (k % kStages) * kStageB; };
+  auto vt = [&](int k) { return lds + (k % kStages) * kStageB + kTileB; };
+  auto issue = [&](int k) {
+    const int nxt = k + kStages - 2;
+    if (nxt < T) issue_tile(d, rm_lds, lds_addr + (nxt % kStages) * kStageB, nxt);
+  };
+  auto wait = [&](int k) {
+    if (k + kStages - 2 < T) wait_vm<2 * (kStages - 3)>();
+    else wait_vm<0>();
+  };
+  // k = 0
+  issue(0);
+  if (NT > 0 && GROUP == 0) {
+    __builtin_amdgcn_s_setprio(1);
+    mfma_phase<NT, false, true>(vt(0), kt(0), f, qf, pf, o_acc, sc);
+    __builtin_amdgcn_s_setprio(0);
+  }
+  __syncthreads();
+  if (NT > 0) {
+    if (GROUP == 0) {
+      softmax_tile<NT>(sc, half, T == 1 ? last_valid : kBN, c, o_acc, m_run, l_run, pf);
+    } else {
+      __builtin_amdgcn_s_setprio(1);
+      mfma_phase<NT, false, true>(vt(0), kt(0), f, qf, pf, o_acc, sc);
+      __builtin_amdgcn_s_setprio(0);
+    }
+  }
+  wait(0);
+  __syncthreads();
+  for (int k = 1; k < T; ++k) {
+    issue(k);
+    if (NT > 0) {
+      if (GROUP == 0) {
+        __builtin_amdgcn_s_setprio(1);
+        mfma_phase<NT, true, true>(vt(k - 1), kt(k), f, qf, pf, o_acc, sc);
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        softmax_tile<NT>(sc, half, kBN, c, o_acc, m_run, l_run, pf);
+      }
+    }
+    __syncthreads();
+    if (NT > 0) {
+      if (GROUP == 0) {
+        softmax_tile<NT>(sc, half, k == T - 1 ? last_valid : kBN, c, o_acc, m_run, l_run,
+                         pf);
+      } else {
+        __builtin_amdgcn_s_setprio(1);
+        mfma_phase<NT, true, true>(vt(k - 1), kt(k), f, qf, pf, o_acc, sc);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+    wait(k);
+    __syncthreads();
+  }
+  // k = T
+  if (NT > 0) {
+    if (GROUP == 0) {
+      __builtin_amdgcn_s_setprio(1);
+      mfma_phase<NT, true, false>(vt(T - 1), kt(T), f, qf, pf, o_acc, sc);
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+      softmax_tile<NT>(sc, half, last_valid, c, o_acc, m_run, l_run, pf);
+    }
+  }
+  __syncthreads();
+  if (NT > 0 && GROUP == 1) {
+    __builtin_amdgcn_s_setprio(1);
+    mfma_phase<NT, true, false>(vt(T - 1), kt(T), f, qf, pf, o_acc, sc);
+    __builtin_amdgcn_s_setprio(0);
+  }
+  __syncthreads();
+}
+
+// A wave's whole key range [t_begin, t_end): in chunks whose row map fits in
+// LDS (one chunk unless the workspace limits the split count); the pipeline
+// drains between chunks, the softmax state carries over.
+template <int NT, int GROUP>
+__device__ __forceinline__ void run_phases(
+    const Dma& d, const uint32_t* rowmap, uint32_t* rm_lds, const char* lds,
+    uint32_t lds_addr, int t_begin, int t_end, uint32_t row_bytes, const Frag& f,
+    int half, float c, const bf16x8 (&qf)[2][4], f32x16 (&o_acc)[2][2], float (&m_run)[2],
+    float (&l_run)[2]) {
+  for (int c0 = t_begin; c0 < t_end; c0 += kRmMax) {
+    const int c1 = min(t_end, c0 + kRmMax);
+    const int T = (c1 - c0 + kBN - 1) / kBN;
+    const int last_valid = c1 - (c0 + (T - 1) * kBN);
+    // Row map -> byte offsets; the map is padded past the last token, so
+    // reading whole tiles stays inside it.
+    const uint32_t* rm = rowmap + c0;
+    for (int i = threadIdx.x * 4; i < T * kBN; i += kThreads * 4) {
+      const uint4 r = *reinterpret_cast<const uint4*>(rm + i);
+      *reinterpret_cast<uint4*>(rm_lds + i) =
+          make_uint4(r.x * row_bytes, r.y * row_bytes, r.z * row_bytes, r.w * row_bytes);
+    }
+    __syncthreads();
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt) {
-    bf16x8 vf[4];
-#pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2)
-      vf[k2] = lds_frag(vt + (32 * dt + col) * kRow + 16 * k2 + 8 * half);
-#pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        o_acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            vf[k2], pf[nt][k2], o_acc[nt][dt], 0, 0, 0);
+    for (int u = 0; u < kStages - 2; ++u)
+      if (u < T) issue_tile(d, rm_lds, lds_addr + u * kStageB, u);
+    wait_vm<0>();
+    __syncthreads();
+    chunk_phases<NT, GROUP>(d, rm_lds, lds, lds_addr, T, last_valid, f, half, c, qf,
+                            o_acc, m_run, l_run);
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a,
-                                                           int n_qtiles,
+__global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a, int n_qtiles,
                                                            int n_items) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kTile];
-
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageB];
+  __shared__ __attribute__((aligned(16))) uint32_t rm_lds[kRmMax];
   // Work item: query tiles of one (head, split) are consecutive items, and a
   // contiguous range of items goes to one XCD.
   const int per_xcd = gridDim.x >> 3;
@@ -254,86 +430,83 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a,
   const int unit = item / n_qtiles;
   const int h = unit % a.num_heads;
   const int split = unit / a.num_heads;
-
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(a.nk, t_begin + a.tokens_per_split);
-  const int n_tiles = (t_end - t_begin + kBN - 1) / kBN;
+  if (t_begin >= t_end) return;  // the launch never makes an empty split
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int col = lane & 31;   // query column inside a 32-wide tile
-  const int half = lane >> 5;  // which 8-element k group / 4-row group
-
-  // Loader role: tokens 4*q4..4*q4+3 of each tile, dims 4*c..4*c+3.
-  const int q4 = tid >> 4;
-  const int c = tid & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
   const size_t hd = size_t(a.num_heads) * kD;
   const uint32_t row_bytes = uint32_t(hd) * 2u;
-  const uint32_t col_bytes = uint32_t(c) * 8u;
-  const char* kbase = reinterpret_cast<const char*>(a.pool) + size_t(h) * kD * 2;
-  const char* vbase = kbase + size_t(a.page_size) * row_bytes;
-  const uint32_t* rm = a.rowmap + t_begin + 4 * q4;
 
-  // Queries of this wave; Q^T fragments as MFMA B operands.
+  Frag f;
+  {
+    // K: lane (col, half) reads row col, chunk 2s + half.
+    const int fk = swz(col & 7);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      f.kofs[s] = uint32_t(col * kRowB + (((2 * s + half) ^ fk) * 16));
+    // V: in 16-lane group q16, lane j addresses key 4*(q16/2) + j/4 (+16
+    // per k-step, +8 for the upper half) and dims 16*(q16&1) + 4*(j&3) of
+    // the 32-dim tile dt, i.e. chunk 4dt + 2*(q16&1) + (j>>1 & 1), byte 8*(j&1).
+    const int q16 = lane >> 4, j = lane & 15;
+    const int r = 4 * (q16 >> 1) + (j >> 2);
+    const int fv = swz(r);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+      f.vofs[dt] = uint32_t(r * kRowB +
+                            (((4 * dt + 2 * (q16 & 1) + ((j >> 1) & 1)) ^ fv) * 16) +
+                            (j & 1) * 8);
+  }
+  Dma d;
+  {
+    const int kv = wave >> 2, wq = wave & 3;
+    d.base = reinterpret_cast<const char*>(a.pool) + size_t(h) * kD * 2 +
+             (kv ? size_t(a.page_size) * row_bytes : 0);
+    d.dst = uint32_t(kv * kTileB + 16 * wq * kRowB);
+    const int r = lane >> 3;
+    d.rm_off = uint32_t(16 * wq + r);
+    d.coff = uint32_t(((lane & 7) ^ swz(r)) * 16);
+  }
+  const uint32_t lds_addr = lds_u32(lds);
+
+  // Queries of this wave: rows q0 .. q0+63 of the frame, as Q^T fragments
+  // (B operands).
   const int q0 = qt * kBM + wave * 64;
   const int n_active = (q0 < a.nq) + (q0 + 32 < a.nq);
+  const float c = a.sm_scale * kLog2e;
   bf16x8 qf[2][4];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int qi = q0 + nt * 32 + col;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (qi < a.nq) {
-        qf[nt][s] = *reinterpret_cast<const bf16x8*>(
-            a.q + size_t(qi) * hd + size_t(h) * kD + 16 * s + 8 * half);
-      } else {
-        qf[nt][s] = bf16x8{};
-      }
+      qf[nt][s] = qi < a.nq ? *reinterpret_cast<const bf16x8*>(
+                                  a.q + size_t(qi) * hd + size_t(h) * kD + 16 * s + 8 * half)
+                            : bf16x8{};
     }
   }
-
   f32x16 o_acc[2][2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) o_acc[nt][dt] = f32x16{};
+  for (int nt = 0; nt < 2; ++nt) o_acc[nt][0] = o_acc[nt][1] = f32x16{};
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
-  const float c2 = a.sm_scale * kLog2e;
 
-  // Prologue: tile 0 into LDS, row ids of tile 1 in registers.  The row map
-  // is padded past the last token, so these reads stay inside it.
-  TileRegs regs;
-  uint4 rid = *reinterpret_cast<const uint4*>(rm);
-  load_tile(kbase, vbase, rid, row_bytes, col_bytes, regs);
-  rid = *reinterpret_cast<const uint4*>(rm + kBN);
-  store_tile(lds, lds + kTile, q4, c, regs);
-  __syncthreads();
-
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
-    const uint16_t* ks = lds + buf * 2 * kTile;
-    const uint16_t* vt = ks + kTile;
-    const bool more = it + 1 < n_tiles;
-    if (more) {
-      load_tile(kbase, vbase, rid, row_bytes, col_bytes, regs);
-      rid = *reinterpret_cast<const uint4*>(rm + (it + 2) * kBN);
-    }
-
-    const int valid = t_end - (t_begin + it * kBN);  // < kBN on the last tile
-    if (n_active == 2) {
-      compute_tile<2>(ks, vt, qf, o_acc, m_run, l_run, valid, c2, col, half);
-    } else if (n_active == 1) {
-      compute_tile<1>(ks, vt, qf, o_acc, m_run, l_run, valid, c2, col, half);
-    }
-
-    if (more) {
-      uint16_t* nks = lds + (buf ^ 1) * 2 * kTile;
-      store_tile(nks, nks + kTile, q4, c, regs);
-    }
-    __syncthreads();
+#define SPKV_RUN(NT, G)                                                                \
+  run_phases<NT, G>(d, a.rowmap, rm_lds, lds, lds_addr, t_begin, t_end, row_bytes, f, half, \
+                    c, qf, o_acc, m_run, l_run)
+  if (wave < 4) {
+    if (n_active == 2) SPKV_RUN(2, 0);
+    else if (n_active == 1) SPKV_RUN(1, 0);
+    else SPKV_RUN(0, 0);
+  } else {
+    if (n_active == 2) SPKV_RUN(2, 1);
+    else if (n_active == 1) SPKV_RUN(1, 1);
+    else SPKV_RUN(0, 1);
   }
+#undef SPKV_RUN
 
   // Epilogue.  Lane (col, half) holds, for d tile dt and register r,
   // d = 32*dt + (r/4)*8 + half*4 + r%4 of query q0 + 32*nt + col.
@@ -351,16 +524,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a,
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int d0 = 32 * dt + rr * 8 + half * 4;
-          __bf16 b0 = (__bf16)(o_acc[nt][dt][4 * rr + 0] * inv);
-          __bf16 b1 = (__bf16)(o_acc[nt][dt][4 * rr + 1] * inv);
-          __bf16 b2 = (__bf16)(o_acc[nt][dt][4 * rr + 2] * inv);
-          __bf16 b3 = (__bf16)(o_acc[nt][dt][4 * rr + 3] * inv);
-          uint2 w;
-          w.x = uint32_t(__builtin_bit_cast(uint16_t, b0)) |
-                (uint32_t(__builtin_bit_cast(uint16_t, b1)) << 16);
-          w.y = uint32_t(__builtin_bit_cast(uint16_t, b2)) |
-                (uint32_t(__builtin_bit_cast(uint16_t, b3)) << 16);
-          *reinterpret_cast<uint2*>(dst + d0) = w;
+          const __bf16 b0 = (__bf16)(o_acc[nt][dt][4 * rr + 0] * inv);
+          const __bf16 b1 = (__bf16)(o_acc[nt][dt][4 * rr + 1] * inv);
+          const __bf16 b2 = (__bf16)(o_acc[nt][dt][4 * rr + 2] * inv);
+          const __bf16 b3 = (__bf16)(o_acc[nt][dt][4 * rr + 3] * inv);
+          uint2 wv;
+          wv.x = uint32_t(__builtin_bit_cast(uint16_t, b0)) |
+                 (uint32_t(__builtin_bit_cast(uint16_t, b1)) << 16);
+          wv.y = uint32_t(__builtin_bit_cast(uint16_t, b2)) |
+                 (uint32_t(__builtin_bit_cast(uint16_t, b3)) << 16);
+          *reinterpret_cast<uint2*>(dst + d0) = wv;
         }
     } else {
       const size_t row = (size_t(split) * a.nq + qi) * a.num_heads + h;
@@ -375,14 +548,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a,
                           o_acc[nt][dt][4 * rr + 2], o_acc[nt][dt][4 * rr + 3]);
         }
       if (half == 0)
-        *reinterpret_cast<float2*>(a.part_ml + row * 2) =
-            make_float2(m_run[nt], l_tot);
+        *reinterpret_cast<float2*>(a.part_ml + row * 2) = make_float2(m_run[nt], l_tot);
     }
   }
 }
 
-// Combine the splits of each (query, head): with m the running maxima (base
-// 2) and l the sums of each split, O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Combine the splits of each (query, head): with m the reference (base 2)
+// and l the sum of each split, O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 // One thread per (query, head, 4 dims).
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
@@ -428,6 +600,7 @@ hipError_t launch_expand(const PlanArgs& p, hipStream_t stream) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
+  if (a.tokens_per_split <= 0 || a.tokens_per_split % kBN) return hipErrorInvalidValue;
   const int n_qtiles = (a.nq + kBM - 1) / kBM;
   const int n_items = n_qtiles * a.num_heads * a.splits;
   const int grid = (n_items + 7) / 8 * 8;

@@ -38,9 +38,12 @@ struct PlanArgs {
   int32_t n_out;            // entries written (nk rounded up, plus padding)
 };
 
-// Key tiles the kernel uses; run() sizes the split from it.
+// Tiles the kernel uses; run() sizes the split from them.  One workgroup
+// (512 threads, 128 KiB of LDS) is resident per CU.
 constexpr int kAttnKeyTile = 64;
-constexpr int kAttnQueryTile = 256;
+constexpr int kAttnQueryTile = 512;
+// Tokens of a split whose row map the kernel stages in LDS at a time.
+constexpr int kAttnRowmapChunk = 16384;
 // Row-map entries written past the visible tokens.
 constexpr int kRowmapPad = 2 * kAttnKeyTile;
 
