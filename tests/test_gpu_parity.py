@@ -174,6 +174,48 @@ def test_edge_cases_nq_scale_and_sharp_keys():
     cache.close()
 
 
+@pytest.mark.parametrize("mode", ["all_far_below", "all_far_above", "mixed"])
+def test_extreme_logits(mode):
+    """Scores far from 0 in base-2 units: every score of a frame below -64
+    (the first tile of each key range must move the reference down), every
+    score above +16 (it must move up before any p is formed), and a mix of
+    frames of both kinds with planted sharp keys.  Three forced key-range
+    splits give several first tiles per run."""
+    need_gpu()
+    wl = MID.with_(name="extreme", num_blocks=1, frames=5, keyframe_interval=1)
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    o = PagePoolOracle(cfg, track_pool=[0])
+    cache = new_cache(wl)
+    cache.set_num_splits(3)
+    n, h, d = wl.tokens_per_frame, wl.num_heads, wl.head_dim
+    u = torch.full((h, d), 2.5, device=DEV)          # |u|^2 = 400 per head
+    gen = torch.Generator(device=DEV).manual_seed(31)
+    for f in range(wl.frames):
+        q, k, v = synth.frame_qkv(wl, f, 0, device=DEV)
+        noise = 0.5 * torch.randn((n, h, d), generator=gen, device=DEV)
+        if mode == "all_far_below":
+            sign = -1.0                              # s * q.k ~ -50: x ~ -72
+        elif mode == "all_far_above":
+            sign = 1.0                               # x ~ +72
+        else:
+            sign = -1.0 if f % 2 else 1.0
+        q = (u + 0.2 * q.float()).to(torch.bfloat16)
+        k = (sign * u + noise).to(torch.bfloat16)
+        if mode == "mixed" and f == 3:
+            k[6 + 40] = (q[0].float() * 1.5).to(torch.bfloat16)
+        cache.append_frame(0, k, v)
+        cache.evict_frames(0, wl.scale_frames, wl.sliding_window)
+        cache.plan()
+        o.append_frame(0, synth.bf16_bits(k), synth.bf16_bits(v))
+        o.evict_frames(0, wl.scale_frames, wl.sliding_window)
+        pl = o.plan()
+        out = cache.run(0, q, sm_scale=0.125)
+        torch.cuda.synchronize()
+        ref = paged_attention(o.pools[0], pl, cfg, synth.bf16_bits(q), 0.125)
+        H.compare(out, ref, ("extreme", mode, f))
+    cache.close()
+
+
 def test_constant_v_is_reproduced():
     need_gpu()
     wl = MID.with_(name="constv", num_blocks=1, frames=4, keyframe_interval=1)
