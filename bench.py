@@ -44,6 +44,8 @@ def parse():
                     help="blocks of the oracle frame timed (scaled to all)")
     ap.add_argument("--no-events", action="store_true",
                     help="time without per-kernel events (roofline omitted)")
+    ap.add_argument("--append-sweep", action="store_true",
+                    help="only measure the append kernel against frame size")
     return ap.parse_args()
 
 
@@ -136,6 +138,59 @@ def cpu_baseline(wl, warm_frames, n_blocks_timed):
     }
 
 
+def append_sweep(reps=40):
+    """Bandwidth of the append kernel against frame size: one block, H=16,
+    D=64, P patch tokens per frame in P-token pages, P from 999 (the 518x378
+    frame, 8.2 MB of K/V read + written per append) up to 256k tokens (2 GB).
+    Pages and source frames rotate through about 1 GB each, so that neither
+    side sits in the 256 MB last-level cache.  Prints one line per size with
+    the event time per append (which includes the launch gap between
+    back-to-back launches); the kernel's own duration comes from a kernel
+    trace of this command."""
+    import torch
+    import streaming_paged_kv_amd as spkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    h, d, ns = 16, 64, 6
+    for p in (999, 1999, 3999, 7999, 15999, 31999, 63999, 127999, 255999):
+        page_bytes = 2 * p * h * d * 2
+        live = max(1, min(254, (1 << 30) // page_bytes))
+        frame_bytes = 2 * (p + ns) * h * d * 2
+        nbank = max(2, min(256, (1 << 30) // frame_bytes))
+        cfg = dict(num_blocks=1, num_heads=h, head_dim=d, page_size=p, patch_tokens=p,
+                   num_special_tokens=ns, scale_frames=1, sliding_window=live, headroom=1,
+                   max_total_frames=max(1, p // ns) * 4)
+        min_ws = spkv.query_sizes(**cfg)[2]
+        cache = spkv.PagedKVCache(**cfg, device=dev, workspace_bytes=min_ws)
+        g = torch.Generator(device=dev).manual_seed(p)
+        src = torch.randn((nbank, 2, p + ns, h, d), generator=g, device=dev).to(torch.bfloat16)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        nbytes = 4 * (p + ns) * h * d * 2
+        nrep = max(reps, min(400, (2 << 30) // nbytes))   # touch >= 2 GB
+        n = 0
+        for r in range(nrep + 5):
+            if cache.get_cache_stats(0)[0] >= max(1, p // ns) * 4:
+                cache.reset()
+            if r == 5:
+                e0.record(stream)
+            f = r % nbank
+            cache.append_frame(0, src[f, 0], src[f, 1], stream=stream)
+            cache.evict_frames(0, 1, live)
+            n += r >= 5
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        print(f"append P={p:6d}: {nbytes:11d} bytes/append, {us:8.2f} us/append by events "
+              f"(launch gaps included), {nbytes / us / 1e3:7.0f} GB/s", flush=True)
+        cache.close()
+        del src, cache
+        torch.cuda.empty_cache()
+
+
 def kernel_hash():
     import hashlib
     with open(ATTN_SRC, "rb") as f:
@@ -166,6 +221,9 @@ def main():
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
+    if args.append_sweep:
+        append_sweep()
+        return
     import torch
     import streaming_paged_kv_amd as spkv
     import synth
