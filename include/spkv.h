@@ -102,8 +102,9 @@ typedef struct spkv_stats {
  *   max_num_pages        = M + ceil(max_total_frames / floor(page_size / ns))
  *   pool_bytes_per_block = max_num_pages * 2 * page_size * H * D * 2
  *   min_workspace_bytes  = the least device workspace create() accepts: the
- *                          double-buffered device page table and its
- *                          per-token expansion (4 bytes per page slot).
+ *                          double-buffered device page table and its two
+ *                          per-token expansions (4 bytes per page slot, the
+ *                          second one frame longer, for run_own).
  *                          run() then processes each (query tile, head) in
  *                          one pass.
  *   full_workspace_bytes = workspace that lets run() split the key range
@@ -193,10 +194,27 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream);
  * positional encoding).  q, out: device [nq][H][D] bf16, contiguous, not
  * overlapping; 1 <= nq <= num_special_tokens + patch_tokens; sm_scale finite
  * and > 0.  NOT_PLANNED before a plan, STALE_PLAN when the block's scale,
- * live and special state differ from block 0's at plan time.  Enqueues the
- * attention kernel (and, when the key range is split, a merge kernel). */
+ * live and special state differ from block 0's at plan time.  UNSUPPORTED
+ * when a block's pool exceeds 4 GiB (pool rows are addressed by 32-bit byte
+ * offsets).  Enqueues the attention kernel (and, when the key range is split,
+ * a merge kernel). */
 SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
                       int32_t nq, float sm_scale, void* hip_stream);
+
+/* run(block) for a frame that attends to the cache without joining it: the
+ * non-keyframe case of [LB-SLOT] "进阶：光流关键帧与回滚机制" (it attends to
+ * the cache plus its own K/V, and its K/V are not stored) and the
+ * configuration's "skip append".  The visible tokens are the plan's, as for
+ * run(), followed by every row of the caller's frame own_k / own_v (device
+ * [num_special_tokens + patch_tokens][H][D] bf16, contiguous, the layout
+ * append_frame takes).  Neither the pool nor any state changes, so there is
+ * nothing to roll back.  Arguments and errors as for run(); own_k and own_v
+ * must not overlap out.  UNSUPPORTED when a block's pool exceeds 2 GiB (run()
+ * itself takes pools up to 4 GiB).  Host-only handles pass NULL own_k and
+ * own_v and get run()'s checks and result. */
+SPKV_API int spkv_run_own(spkv_handle* h, int32_t block, const void* q, void* out,
+                          int32_t nq, float sm_scale, const void* own_k,
+                          const void* own_v, void* hip_stream);
 
 /* Split of the key range across workgroups used by run(): 0 = automatic
  * (default), else a fixed count (clamped to what the workspace and the number

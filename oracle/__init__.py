@@ -44,6 +44,7 @@ from .pagepool import (  # noqa: F401
     PagePoolOracle,
     Plan,
 )
-from .attention import gather_visible, dense_attention, paged_attention  # noqa: F401
+from .attention import (  # noqa: F401
+    gather_visible, dense_attention, paged_attention, paged_attention_with_own)
 from .brute import BruteForceStream  # noqa: F401
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits  # noqa: F401

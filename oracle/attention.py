@@ -72,3 +72,20 @@ def paged_attention(pool, plan, cfg, q_bits, sm_scale, rows=None):
     if rows is not None:
         q = q[np.asarray(rows)]
     return dense_attention(q, k, v, sm_scale)
+
+
+def paged_attention_with_own(pool, plan, cfg, q_bits, own_k_bits, own_v_bits, sm_scale,
+                             rows=None):
+    """What run_own(block) computes: a frame that attends to the cache plus
+    its own K/V without joining the cache ([LB-SLOT] "进阶：光流关键帧与回滚机制":
+    a non-keyframe attends to the cache and to its own K/V, which are then
+    discarded).  The visible set is the plan's tokens followed by every row of
+    the frame's own K/V (its specials, then its patches, as the frame is laid
+    out); the order does not change the softmax, only float64 rounding."""
+    k, v = gather_visible(pool, plan, cfg)
+    k = np.concatenate([k, bf16_bits_to_f64(own_k_bits)], axis=0)
+    v = np.concatenate([v, bf16_bits_to_f64(own_v_bits)], axis=0)
+    q = bf16_bits_to_f64(q_bits)
+    if rows is not None:
+        q = q[np.asarray(rows)]
+    return dense_attention(q, k, v, sm_scale)

@@ -52,7 +52,7 @@ EXPORTED = (
     "spkv_query_sizes", "spkv_create", "spkv_destroy", "spkv_append_frame",
     "spkv_evict_frames", "spkv_set_defer_eviction",
     "spkv_execute_deferred_eviction", "spkv_rollback_last_frame", "spkv_reset",
-    "spkv_plan", "spkv_run", "spkv_set_num_splits", "spkv_get_cache_stats",
+    "spkv_plan", "spkv_run", "spkv_run_own", "spkv_set_num_splits", "spkv_get_cache_stats",
     "spkv_get_plan", "spkv_get_block_state", "spkv_error_string",
 )
 
@@ -105,6 +105,7 @@ def load_library(path=None):
         "spkv_reset": [vp],
         "spkv_plan": [vp, vp],
         "spkv_run": [vp, i32, vp, vp, i32, ctypes.c_float, vp],
+        "spkv_run_own": [vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp],
         "spkv_set_num_splits": [vp, i32],
         "spkv_get_cache_stats": [vp, i32, ctypes.POINTER(Stats)],
         "spkv_get_plan": [vp, pi32, i32, pi32, pi32, pi32],
@@ -288,6 +289,29 @@ class PagedKVCache:
         op = self._frame_tensor(out, "out", n)
         _check(self.lib.spkv_run(self._h, block, qp, op, n, float(sm_scale),
                                  _stream_ptr(stream)), "spkv_run")
+        return out
+
+    def run_own(self, block, q=None, k=None, v=None, out=None, sm_scale=None, nq=None,
+                stream=None):
+        """Attention over the planned pages plus the caller's own frame k, v
+        (the layout append_frame takes), without storing them: a non-keyframe
+        that skips the append."""
+        if sm_scale is None:
+            sm_scale = self.cfg["head_dim"] ** -0.5
+        if self.host_only:
+            n = self.tokens_per_frame if nq is None else nq
+            _check(self.lib.spkv_run_own(self._h, block, None, None, n, sm_scale, None,
+                                         None, None), "spkv_run_own")
+            return None
+        n = q.shape[0] if nq is None else nq
+        qp = self._frame_tensor(q, "q", n)
+        kp = self._frame_tensor(k, "k", self.tokens_per_frame)
+        vp = self._frame_tensor(v, "v", self.tokens_per_frame)
+        if out is None:
+            out = torch.empty_like(q)
+        op = self._frame_tensor(out, "out", n)
+        _check(self.lib.spkv_run_own(self._h, block, qp, op, n, float(sm_scale), kp, vp,
+                                     _stream_ptr(stream)), "spkv_run_own")
         return out
 
     def set_num_splits(self, n):

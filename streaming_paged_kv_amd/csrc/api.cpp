@@ -49,7 +49,7 @@ bool to_geometry(const spkv_config* c, spkv::Geometry* g) {
 
 struct Sizes {
   int64_t max_num_pages, pool_bytes, table_bytes, rowmap_entries,
-      rowmap_bytes, min_ws, per_split, full_ws;
+      rowmap_bytes, rowmap_own_bytes, min_ws, per_split, full_ws;
 };
 
 Sizes sizes_of(const spkv::Geometry& g) {
@@ -63,7 +63,11 @@ Sizes sizes_of(const spkv::Geometry& g) {
   s.rowmap_entries = round_up(int64_t(g.max_num_pages) * g.page_size,
                               spkv::kAttnKeyTile) + spkv::kRowmapPad;
   s.rowmap_bytes = round_up(s.rowmap_entries * 4, kAlign);
-  s.min_ws = 2 * s.table_bytes + 2 * s.rowmap_bytes;
+  // The same plus one frame of the caller's own rows (run_own).
+  s.rowmap_own_bytes =
+      round_up((round_up(int64_t(g.max_num_pages) * g.page_size + g.tokens_per_frame,
+                         spkv::kAttnKeyTile) + spkv::kRowmapPad) * 4, kAlign);
+  s.min_ws = 2 * s.table_bytes + 2 * s.rowmap_bytes + 2 * s.rowmap_own_bytes;
   // Partial O (fp32, D per row) and (m, l) for every (query, head) row.
   const int64_t rows = int64_t(g.tokens_per_frame) * g.num_heads;
   s.per_split = round_up(rows * g.head_dim * 4, kAlign) + round_up(rows * 8, kAlign);
@@ -106,6 +110,7 @@ struct spkv_handle {
   int64_t ws_bytes = 0;
   int32_t* dev_table[2] = {nullptr, nullptr};
   uint32_t* dev_rowmap[2] = {nullptr, nullptr};
+  uint32_t* dev_rowmap_own[2] = {nullptr, nullptr};
   int32_t* stage = nullptr;          // pinned, 2 x max_num_pages
   hipEvent_t copied[2] = {nullptr, nullptr};
   bool copy_pending[2] = {false, false};
@@ -197,6 +202,10 @@ SPKV_API int spkv_create(const spkv_config* cfg, void* const* pool_ptrs,
   h->dev_rowmap[0] = reinterpret_cast<uint32_t*>(h->ws + 2 * sz.table_bytes);
   h->dev_rowmap[1] = reinterpret_cast<uint32_t*>(h->ws + 2 * sz.table_bytes +
                                                  sz.rowmap_bytes);
+  h->dev_rowmap_own[0] = reinterpret_cast<uint32_t*>(h->ws + 2 * sz.table_bytes +
+                                                     2 * sz.rowmap_bytes);
+  h->dev_rowmap_own[1] = reinterpret_cast<uint32_t*>(
+      h->ws + 2 * sz.table_bytes + 2 * sz.rowmap_bytes + sz.rowmap_own_bytes);
   h->partials = h->ws + sz.min_ws;
   const int64_t room = workspace_bytes - sz.min_ws;
   h->max_splits = static_cast<int>(
@@ -334,6 +343,11 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream) {
   pa.nk = static_cast<int32_t>(pv.visible_tokens);
   pa.n_out = static_cast<int32_t>(
       round_up(pv.visible_tokens, spkv::kAttnKeyTile) + spkv::kRowmapPad);
+  pa.rowmap_own = h->dev_rowmap_own[slot];
+  pa.n_own = g.tokens_per_frame;
+  pa.n_out_own = static_cast<int32_t>(
+      round_up(pv.visible_tokens + g.tokens_per_frame, spkv::kAttnKeyTile) +
+      spkv::kRowmapPad);
   if (hipMemcpyAsync(h->dev_table[slot], host, size_t(pv.n_pages) * sizeof(int32_t),
                      hipMemcpyHostToDevice, st) != hipSuccess ||
       hipEventRecord(h->copied[slot], st) != hipSuccess ||
@@ -353,29 +367,49 @@ SPKV_API int spkv_set_num_splits(spkv_handle* h, int32_t num_splits) {
   return SPKV_OK;
 }
 
-SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
-                      int32_t nq, float sm_scale, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+bool overlaps(const void* a, const void* b, size_t bytes_a, size_t bytes_b) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + bytes_b && y < x + bytes_a;
+}
+
+// run() and run_own(): own_k == own_v == nullptr for the planned pages alone.
+int run_impl(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq,
+             float sm_scale, const void* own_k, const void* own_v, void* hip_stream) {
   if (!h) return SPKV_ERR_INVALID_ARG;
+  const bool own = own_k != nullptr || own_v != nullptr;
   if (block < 0 || block >= h->g.num_blocks) return SPKV_ERR_BAD_BLOCK;
   const spkv::Geometry& g = h->g;
   if (nq < 1 || nq > g.tokens_per_frame || !std::isfinite(sm_scale) ||
       !(sm_scale > 0.0f))
     return SPKV_ERR_INVALID_ARG;
   if (h->host_only) {
-    if (q || out) return SPKV_ERR_INVALID_ARG;
+    if (q || out || own) return SPKV_ERR_INVALID_ARG;
   } else {
     if (!q || !out || !aligned16(q) || !aligned16(out)) return SPKV_ERR_INVALID_ARG;
     const size_t bytes = size_t(nq) * g.num_heads * g.head_dim * 2;
-    const char* qb = static_cast<const char*>(q);
-    const char* ob = static_cast<const char*>(out);
-    if (qb < ob + bytes && ob < qb + bytes) return SPKV_ERR_INVALID_ARG;
+    if (overlaps(q, out, bytes, bytes)) return SPKV_ERR_INVALID_ARG;
+    if (own) {
+      if (!own_k || !own_v || !aligned16(own_k) || !aligned16(own_v))
+        return SPKV_ERR_INVALID_ARG;
+      const size_t fb = size_t(g.tokens_per_frame) * g.num_heads * g.head_dim * 2;
+      if (overlaps(out, own_k, bytes, fb) || overlaps(out, own_v, bytes, fb))
+        return SPKV_ERR_INVALID_ARG;
+    }
   }
   const spkv::Status s = h->pool->check_run(block);
   if (s != spkv::Status::ok) return status(s);
   if (h->host_only) return SPKV_ERR_UNSUPPORTED;
 
+  // The kernel addresses pool rows by 32-bit byte offsets, whose top bit
+  // marks the caller's own rows in run_own's map.
+  if (h->sz.pool_bytes > (int64_t(1) << (own ? 31 : 32))) return SPKV_ERR_UNSUPPORTED;
   const spkv::PlanView pv = h->pool->plan_view();
-  const int64_t nk = pv.visible_tokens;
+  const int64_t nk = pv.visible_tokens + (own ? g.tokens_per_frame : 0);
   const int64_t n_ktiles = (nk + spkv::kAttnKeyTile - 1) / spkv::kAttnKeyTile;
   const int64_t n_qtiles = (nq + spkv::kAttnQueryTile - 1) / spkv::kAttnQueryTile;
   int64_t splits;
@@ -396,7 +430,9 @@ SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
   DeviceGuard guard(h->device);
   spkv::AttnArgs a;
   a.pool = static_cast<const uint16_t*>(h->pools[block]);
-  a.rowmap = h->dev_rowmap[h->plan_slot];
+  a.own_k = static_cast<const uint16_t*>(own_k);
+  a.own_v = static_cast<const uint16_t*>(own_v);
+  a.rowmap = own ? h->dev_rowmap_own[h->plan_slot] : h->dev_rowmap[h->plan_slot];
   a.q = static_cast<const uint16_t*>(q);
   a.out = static_cast<uint16_t*>(out);
   const int64_t rows = int64_t(nq) * g.num_heads;
@@ -407,12 +443,30 @@ SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
   a.num_heads = g.num_heads;
   a.page_size = g.page_size;
   a.nk = static_cast<int32_t>(nk);
+  a.n_cached = static_cast<int32_t>(pv.visible_tokens);
   a.splits = static_cast<int32_t>(splits);
   a.tokens_per_split = static_cast<int32_t>(tiles_per_split * spkv::kAttnKeyTile);
   a.sm_scale = sm_scale;
   if (spkv::launch_attention(a, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
     return SPKV_ERR_HIP;
   return SPKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
+                      int32_t nq, float sm_scale, void* hip_stream) {
+  return run_impl(h, block, q, out, nq, sm_scale, nullptr, nullptr, hip_stream);
+}
+
+SPKV_API int spkv_run_own(spkv_handle* h, int32_t block, const void* q, void* out,
+                          int32_t nq, float sm_scale, const void* own_k,
+                          const void* own_v, void* hip_stream) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  if (!h->host_only && (!own_k || !own_v)) return SPKV_ERR_INVALID_ARG;
+  return run_impl(h, block, q, out, nq, sm_scale, own_k, own_v, hip_stream);
 }
 
 SPKV_API int spkv_get_cache_stats(const spkv_handle* h, int32_t block,

@@ -75,24 +75,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSumLimit = 65536.0f;   // bound on a lane's partial row sum
 
 // ------------------------------------------------------------- plan expand
-__global__ __launch_bounds__(256) void expand_kernel(PlanArgs p) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= p.n_out) return;
-  const int tt = min(t, p.nk - 1);
+// Pool row of visible token t (0 <= t < nk) of a plan.
+__device__ __forceinline__ uint32_t plan_row(const PlanArgs& p, int t) {
   const int patch_tokens = p.n_patch * p.patch_len;
   int e, o;
-  if (tt < patch_tokens) {
-    e = tt / p.patch_len;
-    o = tt - e * p.patch_len;
+  if (t < patch_tokens) {
+    e = t / p.patch_len;
+    o = t - e * p.patch_len;
   } else {
-    const int u = tt - patch_tokens;
+    const int u = t - patch_tokens;
     const int k = u / p.special_len;
     e = p.n_patch + k;
     o = u - k * p.special_len;
   }
-  p.rowmap[t] = static_cast<uint32_t>(p.table[e]) * 2u *
-                    static_cast<uint32_t>(p.page_size) +
-                static_cast<uint32_t>(o);
+  return static_cast<uint32_t>(p.table[e]) * 2u * static_cast<uint32_t>(p.page_size) +
+         static_cast<uint32_t>(o);
+}
+
+__global__ __launch_bounds__(256) void expand_kernel(PlanArgs p) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < p.n_out) p.rowmap[t] = plan_row(p, min(t, p.nk - 1));
+  if (t < p.n_out_own)
+    p.rowmap_own[t] = t < p.nk ? plan_row(p, t) : kOwnRow | uint32_t(min(t - p.nk, p.n_own - 1));
 }
 
 // ---------------------------------------------------------------- attention
@@ -107,6 +111,11 @@ __device__ __forceinline__ int swz(int x) { return ((x & 3) << 1) | ((x >> 2) & 
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr)
                : "memory");
+}
+
+// 16 bytes per lane from the 64-bit address addr into LDS at lds_addr + 16 * lane.
+__device__ __forceinline__ void dma16_at(const char* addr, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(lds_addr) : "memory");
 }
 
 // Wait until at most N of this wave's vector-memory loads are outstanding.
@@ -143,6 +152,8 @@ struct Frag {
 // wave w&3 fetches keys 16*(w&3) .. +15 in two loads of 8 keys x 128 B.
 struct Dma {
   const char* base;   // pool + head slice (+ page_size rows for V), uniform
+  const char* own;    // caller's frame + head slice (K or V buffer), uniform
+  int own_tile;       // first tile of the chunk that may hold the caller's rows
   uint32_t dst;       // wave's destination inside a stage, uniform
   uint32_t rm_off;    // lane's key inside a tile
   uint32_t coff;      // lane's source chunk (bytes), chosen by the swizzle
@@ -150,12 +161,20 @@ struct Dma {
 
 // Loads of one tile into a stage.  The staged row map holds byte offsets of
 // pool rows (multiples of 128), so the chunk offset is or-ed in.
+// OWN: the row map ends with rows of the caller's frame (kOwnRow set), which
+// are fetched from its buffers; tiles before d.own_tile hold pool rows only.
+template <bool OWN>
 __device__ __forceinline__ void issue_tile(const Dma& d, const uint32_t* rm_lds,
                                            uint32_t stage_addr, int tile) {
   const uint32_t o0 = rm_lds[tile * kBN + d.rm_off] | d.coff;
   const uint32_t o1 = rm_lds[tile * kBN + d.rm_off + 8] | d.coff;
-  dma16(d.base, o0, stage_addr + d.dst);
-  dma16(d.base, o1, stage_addr + d.dst + 1024u);
+  if (!OWN || tile < d.own_tile) {
+    dma16(d.base, o0, stage_addr + d.dst);
+    dma16(d.base, o1, stage_addr + d.dst + 1024u);
+  } else {
+    dma16_at(((o0 & kOwnRow) ? d.own : d.base) + (o0 & ~kOwnRow), stage_addr + d.dst);
+    dma16_at(((o1 & kOwnRow) ? d.own : d.base) + (o1 & ~kOwnRow), stage_addr + d.dst + 1024u);
+  }
 }
 
 // MFMA phase: O^T += V^T P^T for the previous tile, then S^T = K Q^T for
@@ -305,7 +324,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sc)[2][2], int half, int v
 // k+S-2 into the stage that tile k-2 left, and before the barrier that ends
 // phase 2k+1 it waits for its share of tile k+1.  The first and last
 // iterations are peeled so that the loop body has one MFMA shape.
-template <int NT, int GROUP>
+template <int NT, int GROUP, bool OWN>
 __device__ __forceinline__ void chunk_phases(
     const Dma& d, const uint32_t* rm_lds, const char* lds, uint32_t lds_addr, int T,
     int last_valid, const Frag& f, int half, float c, const bf16x8 (&qf)[2][4],
@@ -316,7 +335,7 @@ __device__ __forceinline__ void chunk_phases(
   auto vt = [&](int k) { return lds + (k % kStages) * kStageB + kTileB; };
   auto issue = [&](int k) {
     const int nxt = k + kStages - 2;
-    if (nxt < T) issue_tile(d, rm_lds, lds_addr + (nxt % kStages) * kStageB, nxt);
+    if (nxt < T) issue_tile<OWN>(d, rm_lds, lds_addr + (nxt % kStages) * kStageB, nxt);
   };
   auto wait = [&](int k) {
     if (k + kStages - 2 < T) wait_vm<2 * (kStages - 3)>();
@@ -388,35 +407,38 @@ __device__ __forceinline__ void chunk_phases(
 // A wave's whole key range [t_begin, t_end): in chunks whose row map fits in
 // LDS (one chunk unless the workspace limits the split count); the pipeline
 // drains between chunks, the softmax state carries over.
-template <int NT, int GROUP>
+template <int NT, int GROUP, bool OWN>
 __device__ __forceinline__ void run_phases(
     const Dma& d, const uint32_t* rowmap, uint32_t* rm_lds, const char* lds,
     uint32_t lds_addr, int t_begin, int t_end, uint32_t row_bytes, const Frag& f,
     int half, float c, const bf16x8 (&qf)[2][4], f32x16 (&o_acc)[2][2], float (&m_run)[2],
-    float (&l_run)[2]) {
+    float (&l_run)[2], int n_cached) {
   for (int c0 = t_begin; c0 < t_end; c0 += kRmMax) {
+    Dma dc = d;
+    dc.own_tile = n_cached > c0 ? (n_cached - c0) / kBN : 0;
     const int c1 = min(t_end, c0 + kRmMax);
     const int T = (c1 - c0 + kBN - 1) / kBN;
     const int last_valid = c1 - (c0 + (T - 1) * kBN);
-    // Row map -> byte offsets; the map is padded past the last token, so
-    // reading whole tiles stays inside it.
+    // Row map -> byte offsets (the kOwnRow mark kept); the map is padded
+    // past the last token, so reading whole tiles stays inside it.
     const uint32_t* rm = rowmap + c0;
+    auto ofs = [&](uint32_t e) { return ((e & ~kOwnRow) * row_bytes) | (e & kOwnRow); };
     for (int i = threadIdx.x * 4; i < T * kBN; i += kThreads * 4) {
       const uint4 r = *reinterpret_cast<const uint4*>(rm + i);
-      *reinterpret_cast<uint4*>(rm_lds + i) =
-          make_uint4(r.x * row_bytes, r.y * row_bytes, r.z * row_bytes, r.w * row_bytes);
+      *reinterpret_cast<uint4*>(rm_lds + i) = make_uint4(ofs(r.x), ofs(r.y), ofs(r.z), ofs(r.w));
     }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kStages - 2; ++u)
-      if (u < T) issue_tile(d, rm_lds, lds_addr + u * kStageB, u);
+      if (u < T) issue_tile<OWN>(dc, rm_lds, lds_addr + u * kStageB, u);
     wait_vm<0>();
     __syncthreads();
-    chunk_phases<NT, GROUP>(d, rm_lds, lds, lds_addr, T, last_valid, f, half, c, qf,
+    chunk_phases<NT, GROUP, OWN>(dc, rm_lds, lds, lds_addr, T, last_valid, f, half, c, qf,
                             o_acc, m_run, l_run);
   }
 }
 
+template <bool OWN>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a, int n_qtiles,
                                                            int n_items) {
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageB];
@@ -465,6 +487,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a, int n_qti
     const int kv = wave >> 2, wq = wave & 3;
     d.base = reinterpret_cast<const char*>(a.pool) + size_t(h) * kD * 2 +
              (kv ? size_t(a.page_size) * row_bytes : 0);
+    d.own = OWN ? reinterpret_cast<const char*>(kv ? a.own_v : a.own_k) + size_t(h) * kD * 2
+                : d.base;
+    d.own_tile = 0;
     d.dst = uint32_t(kv * kTileB + 16 * wq * kRowB);
     const int r = lane >> 3;
     d.rm_off = uint32_t(16 * wq + r);
@@ -495,8 +520,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a, int n_qti
   float l_run[2] = {0.f, 0.f};
 
 #define SPKV_RUN(NT, G)                                                                \
-  run_phases<NT, G>(d, a.rowmap, rm_lds, lds, lds_addr, t_begin, t_end, row_bytes, f, half, \
-                    c, qf, o_acc, m_run, l_run)
+  run_phases<NT, G, OWN>(d, a.rowmap, rm_lds, lds, lds_addr, t_begin, t_end, row_bytes, f, \
+                         half, c, qf, o_acc, m_run, l_run, a.n_cached)
   if (wave < 4) {
     if (n_active == 2) SPKV_RUN(2, 0);
     else if (n_active == 1) SPKV_RUN(1, 0);
@@ -594,8 +619,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 }  // namespace
 
 hipError_t launch_expand(const PlanArgs& p, hipStream_t stream) {
-  hipLaunchKernelGGL(expand_kernel, dim3((p.n_out + 255) / 256), dim3(256), 0,
-                     stream, p);
+  const int n = max(p.n_out, p.n_out_own);
+  hipLaunchKernelGGL(expand_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -604,8 +629,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.nq + kBM - 1) / kBM;
   const int n_items = n_qtiles * a.num_heads * a.splits;
   const int grid = (n_items + 7) / 8 * 8;
-  hipLaunchKernelGGL(attn_kernel, dim3(grid), dim3(kThreads), 0, stream, a,
-                     n_qtiles, n_items);
+  if (a.own_k)
+    hipLaunchKernelGGL(attn_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a,
+                       n_qtiles, n_items);
+  else
+    hipLaunchKernelGGL(attn_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a,
+                       n_qtiles, n_items);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.splits == 1) return err;
   const int rows = a.nq * a.num_heads;

@@ -26,9 +26,19 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // token t, the pool row (page * 2 * page_size + offset) of its K; its V is
 // page_size rows further.  Entries past the last token repeat the last
 // token's row, so a tile that runs past the end reads valid memory.
+//
+// The second map serves runs that also attend to the caller's own frame
+// (run_own): its first nk entries are the same, the next n_own entries are
+// kOwnRow | r for row r of the caller's frame buffers, and entries past them
+// repeat the last of these.
+constexpr uint32_t kOwnRow = 0x80000000u;
+
 struct PlanArgs {
   const int32_t* table;     // device page table, n_pages entries
   uint32_t* rowmap;         // out: n_out entries
+  uint32_t* rowmap_own;     // out: n_out_own entries
+  int32_t n_own;            // rows of a frame (specials + patches)
+  int32_t n_out_own;        // entries written to rowmap_own
   int32_t n_patch, n_pages;
   int32_t patch_len;        // valid tokens of a patch page
   int32_t special_len;      // valid tokens of a full special page
@@ -52,6 +62,8 @@ hipError_t launch_expand(const PlanArgs& p, hipStream_t stream);
 // One attention run over a planned row map.
 struct AttnArgs {
   const uint16_t* pool;     // block's pool (bf16 bits)
+  const uint16_t* own_k;    // caller's frame [n_own][H][D] for kOwnRow rows,
+  const uint16_t* own_v;    //   or null when the map has none
   const uint32_t* rowmap;   // token -> K row of the pool (see PlanArgs)
   const uint16_t* q;        // [nq][H][D]
   uint16_t* out;            // [nq][H][D]
@@ -59,6 +71,7 @@ struct AttnArgs {
   float* part_ml;           // [splits][nq][H][2]     (splits > 1)
   int32_t nq, num_heads, page_size;
   int32_t nk;               // visible tokens
+  int32_t n_cached;         // tokens before the caller's own rows (nk without them)
   int32_t splits, tokens_per_split;
   float sm_scale;
 };

@@ -119,7 +119,7 @@ BIGQ = synth.Workload("bigq", 1, 16, 64, 999, 999, 6, 1, 2, 1, 400, 6,
 
 
 def test_many_query_tiles_and_ragged_query_tail():
-    """1005 query rows = 3 full 256-row tiles plus a 237-row tail."""
+    """1005 query rows = one full 512-row query tile plus a 493-row tail."""
     log("1005 queries, 999-token pages")
     full_parity(BIGQ)
 
@@ -176,11 +176,11 @@ def test_edge_cases_nq_scale_and_sharp_keys():
 
 @pytest.mark.parametrize("mode", ["all_far_below", "all_far_above", "mixed"])
 def test_extreme_logits(mode):
-    """Scores far from 0 in base-2 units: every score of a frame below -64
-    (the first tile of each key range must move the reference down), every
-    score above +16 (it must move up before any p is formed), and a mix of
-    frames of both kinds with planted sharp keys.  Three forced key-range
-    splits give several first tiles per run."""
+    """Scores far from 0: every score of a frame about -50 (every p would
+    underflow unless the reference follows the maximum), every score about
+    +50 (every p would overflow), and a mix of frames of both kinds with a
+    planted sharp key.  Three forced key-range splits give several first
+    tiles per run."""
     need_gpu()
     wl = MID.with_(name="extreme", num_blocks=1, frames=5, keyframe_interval=1)
     cfg = OracleConfig(**wl.cfg_kwargs())
@@ -346,3 +346,96 @@ def test_full_518x378_padded_long_stream():
 
 def test_full_dynamic_stream():
     full_size("dynamic")
+
+
+# ------------------------------------------------- run_own (skip append)
+def own_parity(wl, check_frames=None, rows=None, splits=0):
+    """A stream where keyframes are appended and every non-keyframe attends
+    through run_own over the committed cache plus its own K/V, with no
+    append.  Checked at the chosen non-keyframes: attention against the
+    oracle's definition, and the pool bytes and the allocator state unchanged
+    by run_own."""
+    need_gpu()
+    from oracle.attention import paged_attention_with_own
+    cache = new_cache(wl)
+    if splits:
+        cache.set_num_splits(splits)
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    o = PagePoolOracle(cfg, track_pool=[0])
+    S, W = wl.scale_frames, wl.sliding_window
+    sm = wl.head_dim ** -0.5
+    checked = 0
+    for f in range(wl.frames):
+        q, k, v = synth.frame_qkv(wl, f, 0, device=DEV)
+        if synth.is_keyframe(wl, f):
+            cache.append_frame(0, k, v)
+            cache.evict_frames(0, S, W)
+            cache.plan()
+            cache.run(0, q)
+            o.append_frame(0, synth.bf16_bits(k), synth.bf16_bits(v))
+            o.evict_frames(0, S, W)
+            o.plan()
+            continue
+        if check_frames is not None and f not in check_frames:
+            continue
+        cache.plan()                     # the committed cache, as the last keyframe left it
+        pl = o.plan()
+        before = cache.pools[0].clone()
+        state = cache.get_block_state(0), cache.get_cache_stats(0)
+        out = cache.run_own(0, q, k, v)
+        torch.cuda.synchronize()
+        ref = paged_attention_with_own(o.pools[0], pl, cfg, synth.bf16_bits(q),
+                                       synth.bf16_bits(k), synth.bf16_bits(v), sm, rows=rows)
+        got = out if rows is None else out[rows]
+        H.compare(got, ref, ("run_own", wl.name, f))
+        assert torch.equal(cache.pools[0], before), f
+        assert (cache.get_block_state(0), cache.get_cache_stats(0)) == state, f
+        checked += 1
+        log(f"  run_own frame {f}: {pl.num_visible_tokens(cfg)} cached + "
+            f"{wl.tokens_per_frame} own tokens")
+    cache.close()
+    assert checked > 0
+
+
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_run_own_mid_stream(splits):
+    """203-token pages, interval 2: every non-keyframe through run_own."""
+    log(f"run_own, mid stream, splits={splits}")
+    own_parity(MID.with_(num_blocks=1, frames=24), splits=splits)
+
+
+def test_run_own_tiny_stream_first_frames():
+    """The first non-keyframe sees a single committed frame; 16-token pages."""
+    wl = synth.WORKLOADS["tiny"].with_(keyframe_interval=3, frames=14)
+    log("run_own, tiny stream")
+    own_parity(wl)
+
+
+def test_run_own_518x378_steady_state():
+    """The 518x378 stream on one block up to a full window (72 keyframes),
+    run_own at the first non-keyframes and at steady state, sampled rows."""
+    wl = synth.WORKLOADS["518x378"].with_(num_blocks=1, frames=170)
+    log("run_own, 518x378 one block")
+    own_parity(wl, check_frames={1, 3, 17, 145, 159, 169},
+               rows=H.sample_rows(wl.tokens_per_frame))
+
+
+def test_run_own_rejects_overlap_and_missing_buffers():
+    need_gpu()
+    import streaming_paged_kv_amd as spkv
+    wl = MID.with_(num_blocks=1, frames=2)
+    cache = new_cache(wl)
+    q, k, v = synth.frame_qkv(wl, 0, 0, device=DEV)
+    cache.append_frame(0, k, v)
+    cache.plan()
+    with pytest.raises(spkv.SpkvError) as ei:
+        cache.run_own(0, q, k, v, out=k)           # out overlaps own K
+    assert ei.value.name == "INVALID_ARG"
+    lib = cache.lib
+    import ctypes
+    rc = lib.spkv_run_own(cache._h, 0, ctypes.c_void_p(q.data_ptr()),
+                          ctypes.c_void_p(torch.empty_like(q).data_ptr()), q.shape[0],
+                          0.125, None, ctypes.c_void_p(v.data_ptr()), None)
+    assert rc == -1
+    torch.cuda.synchronize()
+    cache.close()

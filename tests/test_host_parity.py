@@ -65,9 +65,9 @@ def step(o, c, op, block, arg):
         r = (code_of(o.reset), code_of(c.reset))
     elif op == "plan":
         r = (code_of(o.plan), code_of(c.plan))
-    elif op == "run":
+    elif op in ("run", "run_own"):
         ro = code_of(o.check_run, block)
-        rc = code_of(c.run, block)
+        rc = code_of(c.run if op == "run" else c.run_own, block)
         # a host-only handle reports UNSUPPORTED once the checks pass
         r = (ro, "OK" if rc == "UNSUPPORTED" else rc)
     else:
@@ -89,7 +89,7 @@ CFGS = [
 
 op_strategy = st.tuples(
     st.sampled_from(["append", "append", "append", "evict", "evict", "defer",
-                     "execute", "rollback", "plan", "plan", "run", "reset",
+                     "execute", "rollback", "plan", "plan", "run", "run_own", "reset",
                      "evict_badS", "evict_flags"]),
     st.integers(-1, 3), st.integers(0, 6))
 

@@ -60,6 +60,16 @@ def run_stream(cfg, schedule, seed, sm_scale=0.125):
             bf.commit(bf16_bits_to_f64(k), bf16_bits_to_f64(v))
             own = (None, None)
         else:
+            # run_own's definition over the committed cache must give the same
+            # attention as the transient append (same tokens, other order)
+            try:
+                pl0 = o.plan()
+            except OracleError:
+                pl0 = None
+            with_own = None
+            if pl0 is not None:
+                with_own = att.paged_attention_with_own(o.pools[0], pl0, cfg, q, k, v,
+                                                        sm_scale)
             o.set_defer_eviction(True)
             try:
                 o.append_frame(0, k, v)
@@ -75,6 +85,8 @@ def run_stream(cfg, schedule, seed, sm_scale=0.125):
         assert pl.num_visible_tokens(cfg) == nk
         # same tokens in the same order through the same float64 code path
         assert np.array_equal(got, want)
+        if ev != "key" and with_own is not None:
+            np.testing.assert_allclose(with_own, got, rtol=1e-10, atol=1e-12)
         n_cmp += 1
         if ev in ("transient", "reject"):
             o.rollback_last_frame(0)
