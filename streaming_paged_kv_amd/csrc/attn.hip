@@ -580,7 +580,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a, int n_qti
 
 // Combine the splits of each (query, head): with m the reference (base 2)
 // and l the sum of each split, O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One thread per (query, head, 4 dims).
+// One thread per (query, head, 4 dims).  Splits are read eight at a time with
+// all their loads in flight together (this kernel is latency-bound); splits
+// past the count re-read the last one and get weight 0.
+constexpr int kMergeGroup = 8;
+
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     uint16_t* __restrict__ out,
@@ -590,20 +594,36 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   const int d0 = (gid & 15) * 4;
   if (row >= rows) return;
   float mmax = -INFINITY;
-  for (int s = 0; s < splits; ++s)
-    mmax = fmaxf(mmax, part_ml[(size_t(s) * rows + row) * 2]);
+  for (int s0 = 0; s0 < splits; s0 += kMergeGroup) {
+    float mv[kMergeGroup];
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) {
+      const int sj = min(s0 + j, splits - 1);
+      mv[j] = part_ml[(size_t(sj) * rows + row) * 2];
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) mmax = fmaxf(mmax, mv[j]);
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float lsum = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const size_t r = size_t(s) * rows + row;
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + r * 2);
-    const float w = __builtin_amdgcn_exp2f(ml.x - mmax);
-    const float4 ov = *reinterpret_cast<const float4*>(part_o + r * kD + d0);
-    acc.x += w * ov.x;
-    acc.y += w * ov.y;
-    acc.z += w * ov.z;
-    acc.w += w * ov.w;
-    lsum += w * ml.y;
+  for (int s0 = 0; s0 < splits; s0 += kMergeGroup) {
+    float2 ml[kMergeGroup];
+    float4 ov[kMergeGroup];
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) {
+      const size_t r = size_t(min(s0 + j, splits - 1)) * rows + row;
+      ml[j] = *reinterpret_cast<const float2*>(part_ml + r * 2);
+      ov[j] = *reinterpret_cast<const float4*>(part_o + r * kD + d0);
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) {
+      const float w = s0 + j < splits ? __builtin_amdgcn_exp2f(ml[j].x - mmax) : 0.f;
+      acc.x += w * ov[j].x;
+      acc.y += w * ov[j].y;
+      acc.z += w * ov[j].z;
+      acc.w += w * ov[j].w;
+      lsum += w * ml[j].y;
+    }
   }
   const float inv = 1.0f / lsum;
   const __bf16 b0 = (__bf16)(acc.x * inv), b1 = (__bf16)(acc.y * inv);
