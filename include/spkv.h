@@ -192,8 +192,14 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream);
  * and head h,  out[i,h,:] = sum_j softmax_j(sm_scale * q[i,h,:].k[j,h,:]) v[j,h,:]
  * over the visible tokens j of `block` in plan order (non-causal, no
  * positional encoding).  q, out: device [nq][H][D] bf16, contiguous, not
- * overlapping; 1 <= nq <= num_special_tokens + patch_tokens; sm_scale finite
- * and > 0.  NOT_PLANNED before a plan, STALE_PLAN when the block's scale,
+ * overlapping; sm_scale finite and > 0.  nq is one frame's tokens
+ * (num_special_tokens + patch_tokens) or fewer rows of it, or the rows of
+ * several frames at once: the batch mode of the first frames ([LB-KV]
+ * "FlashInferAttention Layer Implementation", Phase 1; [LB-SLOT] scale-frame
+ * section: the first frames attend to one another bidirectionally) is their
+ * appends, one plan and one run with all their queries.  1 <= nq <= 2^20 and
+ * nq * H * D / 4 < 2^31.  The split of the key range is limited by the
+ * workspace: fewer splits for more query rows.  NOT_PLANNED before a plan, STALE_PLAN when the block's scale,
  * live and special state differ from block 0's at plan time.  UNSUPPORTED
  * when a block's pool exceeds 4 GiB (pool rows are addressed by 32-bit byte
  * offsets).  Enqueues the attention kernel (and, when the key range is split,

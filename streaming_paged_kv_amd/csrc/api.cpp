@@ -19,6 +19,10 @@
 namespace {
 
 constexpr int kMaxSplits = 32;
+// Query rows of one run: a frame, or several frames at once (the batch mode
+// of the first frames); bounded so that rows * H and the row offsets stay in
+// 32 bits inside the kernels.
+constexpr int32_t kMaxQueryRows = 1 << 20;
 constexpr int64_t kAlign = 256;
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -117,7 +121,6 @@ struct spkv_handle {
   int plan_slot = 0;                 // slot holding the current plan
   int next_slot = 0;
   char* partials = nullptr;
-  int max_splits = 1;                // what the workspace holds
   int forced_splits = 0;
   int num_cus = 256;
 };
@@ -207,9 +210,6 @@ SPKV_API int spkv_create(const spkv_config* cfg, void* const* pool_ptrs,
   h->dev_rowmap_own[1] = reinterpret_cast<uint32_t*>(
       h->ws + 2 * sz.table_bytes + 2 * sz.rowmap_bytes + sz.rowmap_own_bytes);
   h->partials = h->ws + sz.min_ws;
-  const int64_t room = workspace_bytes - sz.min_ws;
-  h->max_splits = static_cast<int>(
-      std::max<int64_t>(1, std::min<int64_t>(kMaxSplits, room / sz.per_split)));
   if (hipHostMalloc(reinterpret_cast<void**>(&h->stage),
                     size_t(2) * g.max_num_pages * sizeof(int32_t),
                     hipHostMallocDefault) != hipSuccess) {
@@ -384,8 +384,10 @@ int run_impl(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq
   const bool own = own_k != nullptr || own_v != nullptr;
   if (block < 0 || block >= h->g.num_blocks) return SPKV_ERR_BAD_BLOCK;
   const spkv::Geometry& g = h->g;
-  if (nq < 1 || nq > g.tokens_per_frame || !std::isfinite(sm_scale) ||
-      !(sm_scale > 0.0f))
+  if (nq < 1 || nq > kMaxQueryRows || !std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return SPKV_ERR_INVALID_ARG;
+  // the merge runs one thread per (query, head, 4 dims)
+  if (int64_t(nq) * g.num_heads * (g.head_dim / 4) >= (int64_t(1) << 31))
     return SPKV_ERR_INVALID_ARG;
   if (h->host_only) {
     if (q || out || own) return SPKV_ERR_INVALID_ARG;
@@ -422,7 +424,15 @@ int run_impl(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq
     splits = (want + units - 1) / units;
     splits = std::min<int64_t>(splits, std::max<int64_t>(1, n_ktiles / 4));
   }
-  splits = std::max<int64_t>(1, std::min<int64_t>(splits, h->max_splits));
+  // Split partials: fp32 O and (m, l) per (query, head) row and split, in
+  // the workspace after the plan's buffers.
+  const int64_t rows = int64_t(nq) * g.num_heads;
+  auto partial_bytes = [&](int64_t sp) {
+    return round_up(rows * g.head_dim * 4 * sp, kAlign) + round_up(rows * 8 * sp, kAlign);
+  };
+  int64_t cap = kMaxSplits;
+  while (cap > 1 && partial_bytes(cap) > h->ws_bytes - h->sz.min_ws) --cap;
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, cap));
   splits = std::min<int64_t>(splits, n_ktiles);
   const int64_t tiles_per_split = (n_ktiles + splits - 1) / splits;
   splits = (n_ktiles + tiles_per_split - 1) / tiles_per_split;  // none empty
@@ -435,7 +445,6 @@ int run_impl(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq
   a.rowmap = own ? h->dev_rowmap_own[h->plan_slot] : h->dev_rowmap[h->plan_slot];
   a.q = static_cast<const uint16_t*>(q);
   a.out = static_cast<uint16_t*>(out);
-  const int64_t rows = int64_t(nq) * g.num_heads;
   a.part_o = reinterpret_cast<float*>(h->partials);
   a.part_ml = reinterpret_cast<float*>(
       h->partials + round_up(rows * g.head_dim * 4 * splits, kAlign));

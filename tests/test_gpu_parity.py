@@ -439,3 +439,49 @@ def test_run_own_rejects_overlap_and_missing_buffers():
     assert rc == -1
     torch.cuda.synchronize()
     cache.close()
+
+
+# ---------------------------------------------------- batch mode (phase 1)
+def batch_mode_parity(wl, n_frames, rows=None):
+    """The batch mode of the first frames: their K/V appended to every block,
+    one plan, then one run per block with all their queries at once.  The
+    reference is dense bidirectional attention over the frames' tokens
+    concatenated, with no pages involved."""
+    need_gpu()
+    from oracle import bf16_bits_to_f64, dense_attention
+    cache = new_cache(wl)
+    S, W = wl.scale_frames, wl.sliding_window
+    sm = wl.head_dim ** -0.5
+    frames = {b: [synth.frame_qkv(wl, f, b, device=DEV) for f in range(n_frames)]
+              for b in range(wl.num_blocks)}
+    for b in range(wl.num_blocks):
+        for q, k, v in frames[b]:
+            cache.append_frame(b, k, v)
+            cache.evict_frames(b, S, W)
+        if b == 0:
+            cache.plan()
+    for b in range(wl.num_blocks):
+        q_all = torch.cat([x[0] for x in frames[b]]).contiguous()
+        out = cache.run(b, q_all)
+        torch.cuda.synchronize()
+        k_all = bf16_bits_to_f64(synth.bf16_bits(torch.cat([x[1] for x in frames[b]])))
+        v_all = bf16_bits_to_f64(synth.bf16_bits(torch.cat([x[2] for x in frames[b]])))
+        q64 = bf16_bits_to_f64(synth.bf16_bits(q_all))
+        if rows is not None:
+            q64 = q64[rows]
+        ref = dense_attention(q64, k_all, v_all, sm)
+        H.compare(out if rows is None else out[rows], ref, ("batch", wl.name, b))
+        log(f"  batch mode block {b}: {q_all.shape[0]} queries over {k_all.shape[0]} keys")
+    cache.close()
+
+
+def test_batch_mode_tiny_and_mid():
+    batch_mode_parity(synth.WORKLOADS["tiny"], 2)
+    batch_mode_parity(MID.with_(frames=2), 2)
+
+
+def test_batch_mode_518x378_scale_frames():
+    """Eight 1005-token frames at once: 8040 queries over 8040 keys."""
+    wl = synth.WORKLOADS["518x378"].with_(num_blocks=2)
+    rows = sorted(set(H.sample_rows(8 * wl.tokens_per_frame, extra=40)))
+    batch_mode_parity(wl, 8, rows=rows)

@@ -166,3 +166,21 @@ def test_full_stream_schedules_match_oracle(name):
         if f % 50 == 0 or f == frames - 1:
             assert_same(o, c)
     c.close()
+
+
+def test_run_accepts_several_frames_of_queries():
+    """The batch mode of the first frames runs all their queries at once:
+    run() checks nq against its own bound, not against one frame."""
+    import streaming_paged_kv_amd as spkv
+    c = spkv.PagedKVCache(num_blocks=1, num_heads=4, head_dim=64, page_size=16,
+                          patch_tokens=16, num_special_tokens=6, scale_frames=2,
+                          sliding_window=4, headroom=2, max_total_frames=32, host_only=True)
+    for _ in range(2):
+        c.append_frame(0)
+        c.evict_frames(0, 2, 4)
+    c.plan()
+    for nq in (1, 22, 44, 1 << 20):
+        assert code_of(lambda: c.run(0, nq=nq)) == "UNSUPPORTED", nq   # checks passed
+    for nq in (0, (1 << 20) + 1):
+        assert code_of(lambda: c.run(0, nq=nq)) == "INVALID_ARG", nq
+    c.close()
