@@ -67,6 +67,8 @@ Status PagePool::append(int32_t block, AppendResult* out) {
   Block& b = blocks_[block];
   if (b.free_list.empty()) return Status::pool_exhausted;
   if (b.nsf >= g_.special_capacity) return Status::special_overflow;
+  out->prev_last_page = b.last_page;
+  out->prev_last_in_scale = b.last_in_scale;
   const int32_t p = b.free_list.pop_front();
   if (static_cast<int32_t>(b.scale.size()) < g_.scale_frames) {
     b.scale.push_back(p);
@@ -95,7 +97,8 @@ void PagePool::undo_append(int32_t block, const AppendResult& r) {
     b.live.pop_back();
   b.free_list.push_front(r.patch_page);
   b.nsf -= 1;
-  b.last_page = -1;
+  b.last_page = r.prev_last_page;
+  b.last_in_scale = r.prev_last_in_scale;
 }
 
 Status PagePool::check_evict_args(int32_t scale_frames, int32_t window) const {

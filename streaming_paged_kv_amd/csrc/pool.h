@@ -93,6 +93,8 @@ struct AppendResult {
   int32_t patch_page;
   int32_t special_page;
   int32_t special_slot;
+  int32_t prev_last_page;      // rollback target before this append
+  bool prev_last_in_scale;
 };
 
 struct PlanView {
