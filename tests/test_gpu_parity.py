@@ -485,3 +485,80 @@ def test_batch_mode_518x378_scale_frames():
     wl = synth.WORKLOADS["518x378"].with_(num_blocks=2)
     rows = sorted(set(H.sample_rows(8 * wl.tokens_per_frame, extra=40)))
     batch_mode_parity(wl, 8, rows=rows)
+
+
+# ------------------------------------------------------ random schedules
+@pytest.mark.parametrize("seed", [101, 102, 103])
+def test_random_schedules_every_frame(seed):
+    """Seeded random mixes of keyframes, transient (append + rollback)
+    non-keyframes, run_own non-keyframes, deferred accept / reject and resets
+    on a 2-block stream with 16-token pages: after every frame the whole pool,
+    the plan, the stats and the allocator state are bit-exact, and every
+    attention output matches the oracle."""
+    need_gpu()
+    from oracle.attention import paged_attention_with_own
+    rng = np.random.default_rng(seed)
+    wl = synth.WORKLOADS["tiny"].with_(num_blocks=2, frames=40, seed=seed)
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    o = PagePoolOracle(cfg, track_pool=range(wl.num_blocks))
+    cache = new_cache(wl)
+    cache.set_num_splits(int(rng.integers(0, 4)))
+    S, W = wl.scale_frames, wl.sliding_window
+    sm = wl.head_dim ** -0.5
+    nb = wl.num_blocks
+    committed = 0
+    for f in range(wl.frames):
+        ev = rng.choice(["key", "key", "transient", "own", "accept", "reject", "reset"])
+        if ev == "reset" or committed >= 30:       # 32 special slots: stay clear of overflow
+            cache.reset()
+            o.reset()
+            committed = 0
+            if ev == "reset":
+                continue
+            ev = "key"
+        if committed == 0 and ev == "own":
+            ev = "key"                             # run_own needs a committed cache
+        qkv = H.gen_frame(wl, f, nb, DEV)
+        bits = [[synth.bf16_bits(t) for t in x] for x in qkv]
+        if ev == "own":
+            cache.plan()
+            pl = o.plan()
+            for b in range(nb):
+                out = cache.run_own(b, *qkv[b])
+                ref = paged_attention_with_own(o.pools[b], pl, cfg, *bits[b], sm)
+                torch.cuda.synchronize()
+                H.compare(out, ref, ("random", seed, f, ev, b))
+        else:
+            defer = ev != "key"
+            if defer:
+                cache.set_defer_eviction(True)
+                o.set_defer_eviction(True)
+            for b in range(nb):
+                cache.append_frame(b, qkv[b][1], qkv[b][2])
+                o.append_frame(b, bits[b][1], bits[b][2])
+                cache.evict_frames(b, S, W)
+                o.evict_frames(b, S, W)
+                if b == 0:
+                    cache.plan()
+                    o.plan()
+                out = cache.run(b, qkv[b][0])
+                ref = paged_attention(o.pools[b], o.check_run(b), cfg, bits[b][0], sm)
+                torch.cuda.synchronize()
+                H.compare(out, ref, ("random", seed, f, ev, b))
+            for b in range(nb):
+                if ev in ("transient", "reject"):
+                    cache.rollback_last_frame(b)
+                    o.rollback_last_frame(b)
+                elif ev == "accept":
+                    cache.execute_deferred_eviction(b, S, W)
+                    o.execute_deferred_eviction(b, S, W)
+            if defer:
+                cache.set_defer_eviction(False)
+                o.set_defer_eviction(False)
+            committed += ev in ("key", "accept")
+        torch.cuda.synchronize()
+        for b in range(nb):
+            assert list(o.block_state(b)) == list(cache.get_block_state(b)), (seed, f, b)
+            assert tuple(o.get_cache_stats(b)) == cache.get_cache_stats(b), (seed, f, b)
+            assert np.array_equal(synth.bf16_bits(cache.pools[b]), o.pools[b]), (seed, f, b)
+    cache.close()
