@@ -49,6 +49,10 @@ def parse():
                     help="time without per-kernel events (roofline omitted)")
     ap.add_argument("--append-sweep", action="store_true",
                     help="only measure the append kernel against frame size")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="R > 1: R independent streams of the workload, whose "
+                         "attention runs as one run_batch per block, timed against "
+                         "the same streams with one run per stream and block")
     return ap.parse_args()
 
 
@@ -194,6 +198,120 @@ def append_sweep(reps=40):
         torch.cuda.empty_cache()
 
 
+def multi_stream(args, wl, R):
+    """R independent streams of `wl` (each its own cache), advanced frame by
+    frame; per block, every stream appends / evicts / plans as its schedule
+    says, then the R attention requests run either as one run_batch launch or
+    as R separate run() / run_own() calls.  Both modes are timed over the same
+    frames (after the same warmup) and reported with the attention time per
+    block from HIP events around the launches."""
+    import torch
+    import streaming_paged_kv_amd as spkv
+    import synth
+
+    if wl.dynamic or not 1 < R <= spkv.MAX_BATCH:
+        raise SystemExit(f"--streams takes 2..{spkv.MAX_BATCH} on a fixed-schedule workload")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    nb, nq = wl.num_blocks, wl.tokens_per_frame
+    S, W = wl.scale_frames, wl.sliding_window
+    sm = wl.head_dim ** -0.5
+    hd = wl.num_heads * wl.head_dim
+    nbank = max(1, args.bank)
+    bank = [[synth.frame_qkv(wl, f, b, device=dev) for b in range(nb)]
+            for f in range(nbank)]
+    res = {}
+    for mode in ("batched", "separate"):
+        caches = [spkv.PagedKVCache(**wl.cfg_kwargs(), device=dev) for _ in range(R)]
+        outs = [[torch.empty((nq, wl.num_heads, wl.head_dim), dtype=torch.bfloat16,
+                             device=dev) for _ in range(nb)] for _ in range(R)]
+        total = args.warmup + 2 * args.steps
+        sched = frame_schedule(wl, total)
+        ev, flops = [], []
+
+        def visible(c):
+            tab, npatch, lpl = c.get_plan()
+            return (npatch * wl.patch_tokens + (len(tab) - npatch - 1) *
+                    wl.num_special_tokens * (wl.page_size // wl.num_special_tokens) + lpl)
+
+        def step(f, events):
+            key = sched[f] == "key"
+            for b in range(nb):
+                reqs = []
+                for r, c in enumerate(caches):
+                    q, k, v = bank[(f + r) % nbank][b]
+                    if key:
+                        c.append_frame(b, k, v, stream=stream)
+                        c.evict_frames(b, S, W)
+                        if b == 0:
+                            c.plan(stream=stream)
+                        reqs.append(dict(cache=c, block=b, q=q, out=outs[r][b], sm_scale=sm))
+                    else:
+                        reqs.append(dict(cache=c, block=b, q=q, k=k, v=v, out=outs[r][b],
+                                         sm_scale=sm))
+                if events:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                if mode == "batched":
+                    spkv.run_batch(reqs, stream=stream)
+                else:
+                    for rq in reqs:
+                        c = rq["cache"]
+                        if key:
+                            c.run(b, rq["q"], out=rq["out"], sm_scale=sm, stream=stream)
+                        else:
+                            c.run_own(b, rq["q"], rq["k"], rq["v"], out=rq["out"],
+                                      sm_scale=sm, stream=stream)
+                if events:
+                    e1.record(stream)
+                    ev.append((e0, e1))
+                    flops.append(sum(4.0 * nq * (visible(c) + (0 if key else nq)) * hd
+                                     for c in caches))
+
+        for f in range(args.warmup):
+            step(f, False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for f in range(args.warmup, args.warmup + args.steps):
+            step(f, False)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        for f in range(args.warmup + args.steps, total):
+            step(f, True)
+        torch.cuda.synchronize()
+        t_attn = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+        achieved = sum(flops) / sum(t_attn) / 1e12
+        res[mode] = {
+            "frames_per_s": R * args.steps / dt,
+            "ms_per_step": dt / args.steps * 1e3,
+            "attention_us_per_block": sum(t_attn) / len(t_attn) * 1e6,
+            "attention_tflops": achieved,
+            "attention_frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,
+        }
+        for c in caches:
+            c.close()
+        del caches, outs
+        torch.cuda.empty_cache()
+    print(json.dumps({
+        "metric": f"streamed frames/s over {R} independent streams (all streams' frames)",
+        "value": res["batched"]["frames_per_s"],
+        "unit": "frames/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": res["batched"]["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{R} x {wl.name}: {nb} blocks, H={wl.num_heads}, "
+                               f"page_size={wl.page_size}, {nq} tokens/frame, "
+                               f"keyframe_interval={wl.keyframe_interval}; per block one "
+                               f"run_batch over the {R} streams",
+                   "input_bank_frames": nbank},
+        "batched": res["batched"],
+        "separate": res["separate"],
+    }), flush=True)
+
+
 def kernel_hash():
     import hashlib
     with open(ATTN_SRC, "rb") as f:
@@ -226,6 +344,10 @@ def main():
         sys.exit(2)
     if args.append_sweep:
         append_sweep()
+        return
+    if args.streams > 1:
+        import synth
+        multi_stream(args, synth.WORKLOADS[args.workload], args.streams)
         return
     import torch
     import streaming_paged_kv_amd as spkv

@@ -222,6 +222,42 @@ SPKV_API int spkv_run_own(spkv_handle* h, int32_t block, const void* q, void* ou
                           int32_t nq, float sm_scale, const void* own_k,
                           const void* own_v, void* hip_stream);
 
+/* One request of run_batch(): a run() (own_k == own_v == NULL) or a
+ * run_own() of one stream's handle, with that call's arguments. */
+typedef struct {
+  spkv_handle* handle;
+  int32_t block;
+  int32_t nq;
+  const void* q;       /* device [nq][H][D] bf16 */
+  void* out;           /* device [nq][H][D] bf16 */
+  const void* own_k;   /* NULL, or the caller's frame as for run_own() */
+  const void* own_v;
+  float sm_scale;
+} spkv_request;
+
+#define SPKV_MAX_BATCH 16
+
+/* Several independent streams in one launch.  The pages' attention is a
+ * batched prefill over paged K/V whose plan takes per-request query and page
+ * offsets (qo_indptr, paged_kv_indptr) so that one launch serves every
+ * request ([LB-KV] "Kernel-Level Execution Flow"; the pages run one request
+ * per manager), and they advise batching plans where latency allows
+ * ([LB-PERF] "Practical Performance Tuning").  Here each stream keeps its own
+ * handle and plan, and this call runs one request of each.  Each request is
+ * what run() -- or run_own() when own_k and own_v are set -- of its handle
+ * would compute, with the same checks and errors, on its handle's current
+ * plan; results equal those calls' up to the order of floating-point
+ * additions (the key range may be split differently).
+ * 1 <= n <= SPKV_MAX_BATCH; every handle at most once (its workspace holds
+ * its request's split partials); all handles of one device and all host-only
+ * or none; no request's out may overlap another request's q, out, own_k or
+ * own_v.  The key ranges are split so that the work items of all requests
+ * are about equally long and fill the CUs once.  Nothing is enqueued unless
+ * every request passes its checks: the first failing request's code is
+ * returned (host-only handles: UNSUPPORTED after the checks).  Enqueues one
+ * attention kernel and, if any range is split, one merge kernel. */
+SPKV_API int spkv_run_batch(const spkv_request* reqs, int32_t n, void* hip_stream);
+
 /* Split of the key range across workgroups used by run(): 0 = automatic
  * (default), else a fixed count (clamped to what the workspace and the number
  * of key tiles allow).  For tests and tuning. */

@@ -52,7 +52,8 @@ EXPORTED = (
     "spkv_query_sizes", "spkv_create", "spkv_destroy", "spkv_append_frame",
     "spkv_evict_frames", "spkv_set_defer_eviction",
     "spkv_execute_deferred_eviction", "spkv_rollback_last_frame", "spkv_reset",
-    "spkv_plan", "spkv_run", "spkv_run_own", "spkv_set_num_splits", "spkv_get_cache_stats",
+    "spkv_plan", "spkv_run", "spkv_run_own", "spkv_run_batch", "spkv_set_num_splits",
+    "spkv_get_cache_stats",
     "spkv_get_plan", "spkv_get_block_state", "spkv_error_string",
 )
 
@@ -69,6 +70,17 @@ class Config(ctypes.Structure):
         "num_blocks", "num_heads", "head_dim", "page_size", "patch_tokens",
         "num_special_tokens", "scale_frames", "sliding_window", "headroom",
         "max_total_frames")]
+
+
+class Request(ctypes.Structure):
+    """spkv_request: one stream's run (or run_own) inside spkv_run_batch."""
+    _fields_ = [("handle", ctypes.c_void_p), ("block", ctypes.c_int32),
+                ("nq", ctypes.c_int32), ("q", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("own_k", ctypes.c_void_p), ("own_v", ctypes.c_void_p),
+                ("sm_scale", ctypes.c_float)]
+
+
+MAX_BATCH = 16
 
 
 class Stats(ctypes.Structure):
@@ -106,6 +118,7 @@ def load_library(path=None):
         "spkv_plan": [vp, vp],
         "spkv_run": [vp, i32, vp, vp, i32, ctypes.c_float, vp],
         "spkv_run_own": [vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp],
+        "spkv_run_batch": [ctypes.POINTER(Request), i32, vp],
         "spkv_set_num_splits": [vp, i32],
         "spkv_get_cache_stats": [vp, i32, ctypes.POINTER(Stats)],
         "spkv_get_plan": [vp, pi32, i32, pi32, pi32, pi32],
@@ -344,3 +357,45 @@ class PagedKVCache:
                                              ctypes.byref(nf), ctypes.byref(nsf)),
                "spkv_get_block_state")
         return list(sc[:ns.value]), list(lv[:nl.value]), list(fr[:nf.value]), nsf.value
+
+
+def run_batch(requests, stream=None):
+    """Several streams' runs in one launch (spkv_run_batch).
+
+    requests: sequence of dicts with keys cache (a PagedKVCache), block, q and
+    optionally out, k and v (the caller's own frame, as for run_own), sm_scale
+    and nq.  Host-only caches pass no tensors.  Returns the outputs, in order
+    (None for host-only caches).
+    """
+    requests = list(requests)
+    lib = load_library()
+    arr = (Request * max(1, len(requests)))()
+    outs = []
+    host_only = not requests or requests[0]["cache"].host_only
+    for i, r in enumerate(requests):
+        c = r["cache"]
+        sm = r.get("sm_scale")
+        if sm is None:
+            sm = c.cfg["head_dim"] ** -0.5
+        arr[i].handle = c._h
+        arr[i].block = r["block"]
+        arr[i].sm_scale = float(sm)
+        if c.host_only:
+            arr[i].nq = c.tokens_per_frame if r.get("nq") is None else r["nq"]
+            outs.append(None)
+            continue
+        q = r["q"]
+        n = q.shape[0] if r.get("nq") is None else r["nq"]
+        arr[i].nq = n
+        arr[i].q = c._frame_tensor(q, "q", n)
+        out = r.get("out")
+        if out is None:
+            out = torch.empty_like(q)
+        arr[i].out = c._frame_tensor(out, "out", n)
+        if r.get("k") is not None or r.get("v") is not None:
+            arr[i].own_k = c._frame_tensor(r.get("k"), "k", c.tokens_per_frame)
+            arr[i].own_v = c._frame_tensor(r.get("v"), "v", c.tokens_per_frame)
+        outs.append(out)
+    s = None if host_only else _stream_ptr(stream)
+    _check(lib.spkv_run_batch(arr, len(requests), s), "spkv_run_batch")
+    return outs

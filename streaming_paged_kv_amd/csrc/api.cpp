@@ -377,9 +377,15 @@ bool overlaps(const void* a, const void* b, size_t bytes_a, size_t bytes_b) {
   return x < y + bytes_b && y < x + bytes_a;
 }
 
-// run() and run_own(): own_k == own_v == nullptr for the planned pages alone.
-int run_impl(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq,
-             float sm_scale, const void* own_k, const void* own_v, void* hip_stream) {
+// Key tiles of a request after its checks.
+struct RunShape {
+  int64_t nk, n_ktiles, units;  // units = query tiles x heads
+};
+
+// Checks of run() and run_own() (own_k == own_v == nullptr for the planned
+// pages alone) that need no split decision; fills *shape.
+int check_run(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq,
+              float sm_scale, const void* own_k, const void* own_v, RunShape* shape) {
   if (!h) return SPKV_ERR_INVALID_ARG;
   const bool own = own_k != nullptr || own_v != nullptr;
   if (block < 0 || block >= h->g.num_blocks) return SPKV_ERR_BAD_BLOCK;
@@ -411,19 +417,19 @@ int run_impl(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq
   // marks the caller's own rows in run_own's map.
   if (h->sz.pool_bytes > (int64_t(1) << (own ? 31 : 32))) return SPKV_ERR_UNSUPPORTED;
   const spkv::PlanView pv = h->pool->plan_view();
-  const int64_t nk = pv.visible_tokens + (own ? g.tokens_per_frame : 0);
-  const int64_t n_ktiles = (nk + spkv::kAttnKeyTile - 1) / spkv::kAttnKeyTile;
-  const int64_t n_qtiles = (nq + spkv::kAttnQueryTile - 1) / spkv::kAttnQueryTile;
-  int64_t splits;
-  if (h->forced_splits > 0) {
-    splits = h->forced_splits;
-  } else {
-    // One resident workgroup per CU; each split keeps >= 4 key tiles.
-    const int64_t want = int64_t(h->num_cus);
-    const int64_t units = n_qtiles * g.num_heads;
-    splits = (want + units - 1) / units;
-    splits = std::min<int64_t>(splits, std::max<int64_t>(1, n_ktiles / 4));
-  }
+  shape->nk = pv.visible_tokens + (own ? g.tokens_per_frame : 0);
+  shape->n_ktiles = (shape->nk + spkv::kAttnKeyTile - 1) / spkv::kAttnKeyTile;
+  shape->units = (nq + spkv::kAttnQueryTile - 1) / spkv::kAttnQueryTile * g.num_heads;
+  return SPKV_OK;
+}
+
+// Kernel arguments of a checked request with `want` splits of its key range
+// (before the limits of the workspace and of the key tiles).
+spkv::AttnArgs make_run(spkv_handle* h, int32_t block, const void* q, void* out,
+                        int32_t nq, float sm_scale, const void* own_k, const void* own_v,
+                        const RunShape& shape, int64_t want) {
+  const spkv::Geometry& g = h->g;
+  int64_t splits = h->forced_splits > 0 ? h->forced_splits : want;
   // Split partials: fp32 O and (m, l) per (query, head) row and split, in
   // the workspace after the plan's buffers.
   const int64_t rows = int64_t(nq) * g.num_heads;
@@ -433,11 +439,11 @@ int run_impl(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq
   int64_t cap = kMaxSplits;
   while (cap > 1 && partial_bytes(cap) > h->ws_bytes - h->sz.min_ws) --cap;
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, cap));
-  splits = std::min<int64_t>(splits, n_ktiles);
-  const int64_t tiles_per_split = (n_ktiles + splits - 1) / splits;
-  splits = (n_ktiles + tiles_per_split - 1) / tiles_per_split;  // none empty
+  splits = std::min<int64_t>(splits, shape.n_ktiles);
+  const int64_t tiles_per_split = (shape.n_ktiles + splits - 1) / splits;
+  splits = (shape.n_ktiles + tiles_per_split - 1) / tiles_per_split;  // none empty
 
-  DeviceGuard guard(h->device);
+  const bool own = own_k != nullptr;
   spkv::AttnArgs a;
   a.pool = static_cast<const uint16_t*>(h->pools[block]);
   a.own_k = static_cast<const uint16_t*>(own_k);
@@ -451,15 +457,35 @@ int run_impl(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq
   a.nq = nq;
   a.num_heads = g.num_heads;
   a.page_size = g.page_size;
-  a.nk = static_cast<int32_t>(nk);
-  a.n_cached = static_cast<int32_t>(pv.visible_tokens);
+  a.nk = static_cast<int32_t>(shape.nk);
+  a.n_cached = static_cast<int32_t>(shape.nk - (own ? g.tokens_per_frame : 0));
   a.splits = static_cast<int32_t>(splits);
   a.tokens_per_split = static_cast<int32_t>(tiles_per_split * spkv::kAttnKeyTile);
   a.sm_scale = sm_scale;
+  return a;
+}
+
+int run_impl(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq,
+             float sm_scale, const void* own_k, const void* own_v, void* hip_stream) {
+  RunShape shape;
+  const int rc = check_run(h, block, q, out, nq, sm_scale, own_k, own_v, &shape);
+  if (rc != SPKV_OK) return rc;
+  // One resident workgroup per CU; each split keeps >= 4 key tiles.
+  int64_t want = (int64_t(h->num_cus) + shape.units - 1) / shape.units;
+  want = std::min<int64_t>(want, std::max<int64_t>(1, shape.n_ktiles / 4));
+  const spkv::AttnArgs a =
+      make_run(h, block, q, out, nq, sm_scale, own_k, own_v, shape, want);
+  DeviceGuard guard(h->device);
   if (spkv::launch_attention(a, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
     return SPKV_ERR_HIP;
   return SPKV_OK;
 }
+
+// Bytes a request reads (q, and own_k / own_v when set) and writes (out).
+struct Extent {
+  const void* p;
+  size_t bytes;
+};
 
 }  // namespace
 
@@ -476,6 +502,82 @@ SPKV_API int spkv_run_own(spkv_handle* h, int32_t block, const void* q, void* ou
   if (!h) return SPKV_ERR_INVALID_ARG;
   if (!h->host_only && (!own_k || !own_v)) return SPKV_ERR_INVALID_ARG;
   return run_impl(h, block, q, out, nq, sm_scale, own_k, own_v, hip_stream);
+}
+
+SPKV_API int spkv_run_batch(const spkv_request* reqs, int32_t n, void* hip_stream) {
+  if (!reqs || n < 1 || n > SPKV_MAX_BATCH) return SPKV_ERR_INVALID_ARG;
+  static_assert(SPKV_MAX_BATCH <= spkv::kMaxBatchRuns, "batch capacity");
+  for (int32_t i = 0; i < n; ++i) {
+    const spkv_request& r = reqs[i];
+    if (!r.handle) return SPKV_ERR_INVALID_ARG;
+    if ((r.own_k == nullptr) != (r.own_v == nullptr) && !r.handle->host_only)
+      return SPKV_ERR_INVALID_ARG;
+    // Each stream's split partials live in its own workspace: one request
+    // per handle.  All handles drive one device and kind.
+    for (int32_t j = 0; j < i; ++j)
+      if (reqs[j].handle == r.handle) return SPKV_ERR_INVALID_ARG;
+    if (r.handle->host_only != reqs[0].handle->host_only ||
+        r.handle->device != reqs[0].handle->device)
+      return SPKV_ERR_INVALID_ARG;
+  }
+  // No request may write what another one reads or writes.
+  if (!reqs[0].handle->host_only) {
+    for (int32_t i = 0; i < n; ++i) {
+      const spkv::Geometry& gi = reqs[i].handle->g;
+      const size_t out_bytes = size_t(reqs[i].nq > 0 ? reqs[i].nq : 0) * gi.num_heads *
+                               gi.head_dim * 2;
+      for (int32_t j = 0; j < n; ++j) {
+        if (j == i) continue;
+        const spkv::Geometry& gj = reqs[j].handle->g;
+        const size_t qb = size_t(reqs[j].nq > 0 ? reqs[j].nq : 0) * gj.num_heads *
+                          gj.head_dim * 2;
+        const size_t fb = size_t(gj.tokens_per_frame) * gj.num_heads * gj.head_dim * 2;
+        const Extent ext[4] = {{reqs[j].q, qb}, {reqs[j].out, qb},
+                               {reqs[j].own_k, fb}, {reqs[j].own_v, fb}};
+        for (const Extent& e : ext)
+          if (reqs[i].out && e.p && overlaps(reqs[i].out, e.p, out_bytes, e.bytes))
+            return SPKV_ERR_INVALID_ARG;
+      }
+    }
+  }
+  RunShape shape[SPKV_MAX_BATCH];
+  const bool host_only = reqs[0].handle->host_only;
+  for (int32_t i = 0; i < n; ++i) {
+    const spkv_request& r = reqs[i];
+    const int rc = check_run(r.handle, r.block, r.q, r.out, r.nq, r.sm_scale, r.own_k,
+                             r.own_v, &shape[i]);
+    // a host-only handle passes every check and then reports UNSUPPORTED
+    if (rc != SPKV_OK && !(host_only && rc == SPKV_ERR_UNSUPPORTED)) return rc;
+  }
+  if (host_only) return SPKV_ERR_UNSUPPORTED;
+  // Batch plan: split each request's key range so that every work item
+  // (query tile x head x split) covers at most per_item key tiles, with the
+  // smallest per_item (>= 4) whose items still fit the CUs once.
+  const int64_t cus = reqs[0].handle->num_cus;
+  int64_t work = 0, max_tiles = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    work += shape[i].units * shape[i].n_ktiles;
+    max_tiles = std::max(max_tiles, shape[i].n_ktiles);
+  }
+  auto items_at = [&](int64_t per) {
+    int64_t items = 0;
+    for (int32_t i = 0; i < n; ++i) items += shape[i].units * ((shape[i].n_ktiles + per - 1) / per);
+    return items;
+  };
+  int64_t per_item = std::max<int64_t>(4, (work + cus - 1) / cus);
+  while (per_item < max_tiles && items_at(per_item) > cus) ++per_item;
+  spkv::AttnArgs runs[SPKV_MAX_BATCH];
+  for (int32_t i = 0; i < n; ++i) {
+    const spkv_request& r = reqs[i];
+    const int64_t want = (shape[i].n_ktiles + per_item - 1) / per_item;
+    runs[i] = make_run(r.handle, r.block, r.q, r.out, r.nq, r.sm_scale, r.own_k, r.own_v,
+                       shape[i], want);
+  }
+  DeviceGuard guard(reqs[0].handle->device);
+  if (spkv::launch_attention_batch(runs, n, static_cast<hipStream_t>(hip_stream)) !=
+      hipSuccess)
+    return SPKV_ERR_HIP;
+  return SPKV_OK;
 }
 
 SPKV_API int spkv_get_cache_stats(const spkv_handle* h, int32_t block,

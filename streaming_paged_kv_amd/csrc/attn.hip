@@ -438,16 +438,32 @@ __device__ __forceinline__ void run_phases(
   }
 }
 
-template <bool OWN>
-__global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a, int n_qtiles,
-                                                           int n_items) {
+// The runs of one launch (several only when independent streams are batched):
+// run r owns work items [item_end[r-1], item_end[r]); entries past the last
+// run repeat the total.
+template <int NB>
+struct Runs {
+  int32_t n_items;
+  int32_t item_end[NB];
+  int32_t n_qtiles[NB];
+  AttnArgs a[NB];
+};
+
+template <bool OWN, int NB>
+__global__ __launch_bounds__(kThreads, 1) void attn_kernel(const Runs<NB> runs) {
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageB];
   __shared__ __attribute__((aligned(16))) uint32_t rm_lds[kRmMax];
   // Work item: query tiles of one (head, split) are consecutive items, and a
   // contiguous range of items goes to one XCD.
   const int per_xcd = gridDim.x >> 3;
-  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (item >= n_items) return;
+  int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (item >= runs.n_items) return;
+  int ri = 0;
+#pragma unroll
+  for (int r = 0; r < NB - 1; ++r) ri += item >= runs.item_end[r];
+  if (NB > 1 && ri > 0) item -= runs.item_end[ri - 1];
+  const AttnArgs& a = runs.a[ri];
+  const int n_qtiles = runs.n_qtiles[ri];
   const int qt = item % n_qtiles;
   const int unit = item / n_qtiles;
   const int h = unit % a.num_heads;
@@ -487,7 +503,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a, int n_qti
     const int kv = wave >> 2, wq = wave & 3;
     d.base = reinterpret_cast<const char*>(a.pool) + size_t(h) * kD * 2 +
              (kv ? size_t(a.page_size) * row_bytes : 0);
-    d.own = OWN ? reinterpret_cast<const char*>(kv ? a.own_v : a.own_k) + size_t(h) * kD * 2
+    d.own = OWN && a.own_k
+                ? reinterpret_cast<const char*>(kv ? a.own_v : a.own_k) + size_t(h) * kD * 2
                 : d.base;
     d.own_tile = 0;
     d.dst = uint32_t(kv * kTileB + 16 * wq * kRowB);
@@ -585,11 +602,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a, int n_qti
 // past the count re-read the last one and get weight 0.
 constexpr int kMergeGroup = 8;
 
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml,
-                                                    uint16_t* __restrict__ out,
-                                                    int rows, int splits) {
-  const int gid = blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
+                                         const float* __restrict__ part_ml,
+                                         uint16_t* __restrict__ out, int rows, int splits,
+                                         int gid) {
   const int row = gid >> 4;   // (query, head) flattened
   const int d0 = (gid & 15) * 4;
   if (row >= rows) return;
@@ -636,6 +652,35 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   *reinterpret_cast<uint2*>(out + size_t(row) * kD + d0) = w;
 }
 
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml,
+                                                    uint16_t* __restrict__ out,
+                                                    int rows, int splits) {
+  merge_row(part_o, part_ml, out, rows, splits, blockIdx.x * 256 + threadIdx.x);
+}
+
+// The split runs of a batched launch: run r owns merge blocks
+// [end_block[r-1], end_block[r]); entries past the last run repeat the total.
+template <int NB>
+struct Merges {
+  int32_t end_block[NB];
+  int32_t rows[NB], splits[NB];
+  const float* part_o[NB];
+  const float* part_ml[NB];
+  uint16_t* out[NB];
+};
+
+template <int NB>
+__global__ __launch_bounds__(256) void merge_batch_kernel(const Merges<NB> m) {
+  const int blk = blockIdx.x;
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i) r += blk >= m.end_block[i];
+  const int b0 = r > 0 ? m.end_block[r - 1] : 0;
+  merge_row(m.part_o[r], m.part_ml[r], m.out[r], m.rows[r], m.splits[r],
+            (blk - b0) * 256 + int(threadIdx.x));
+}
+
 }  // namespace
 
 hipError_t launch_expand(const PlanArgs& p, hipStream_t stream) {
@@ -646,21 +691,66 @@ hipError_t launch_expand(const PlanArgs& p, hipStream_t stream) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   if (a.tokens_per_split <= 0 || a.tokens_per_split % kBN) return hipErrorInvalidValue;
-  const int n_qtiles = (a.nq + kBM - 1) / kBM;
-  const int n_items = n_qtiles * a.num_heads * a.splits;
-  const int grid = (n_items + 7) / 8 * 8;
+  Runs<1> r;
+  r.n_qtiles[0] = (a.nq + kBM - 1) / kBM;
+  r.n_items = r.item_end[0] = r.n_qtiles[0] * a.num_heads * a.splits;
+  r.a[0] = a;
+  const int grid = (r.n_items + 7) / 8 * 8;
   if (a.own_k)
-    hipLaunchKernelGGL(attn_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a,
-                       n_qtiles, n_items);
+    hipLaunchKernelGGL((attn_kernel<true, 1>), dim3(grid), dim3(kThreads), 0, stream, r);
   else
-    hipLaunchKernelGGL(attn_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a,
-                       n_qtiles, n_items);
+    hipLaunchKernelGGL((attn_kernel<false, 1>), dim3(grid), dim3(kThreads), 0, stream, r);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.splits == 1) return err;
   const int rows = a.nq * a.num_heads;
   const int threads = rows * 16;
   hipLaunchKernelGGL(merge_kernel, dim3((threads + 255) / 256), dim3(256), 0,
                      stream, a.part_o, a.part_ml, a.out, rows, a.splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_batch(const AttnArgs* runs, int n, hipStream_t stream) {
+  if (n < 1 || n > kMaxBatchRuns) return hipErrorInvalidValue;
+  if (n == 1) return launch_attention(runs[0], stream);
+  constexpr int NB = kMaxBatchRuns;
+  Runs<NB> r{};
+  Merges<NB> m{};
+  bool own = false;
+  int items = 0, blocks = 0, n_merge = 0;
+  for (int i = 0; i < n; ++i) {
+    const AttnArgs& a = runs[i];
+    if (a.tokens_per_split <= 0 || a.tokens_per_split % kBN) return hipErrorInvalidValue;
+    r.n_qtiles[i] = (a.nq + kBM - 1) / kBM;
+    items += r.n_qtiles[i] * a.num_heads * a.splits;
+    r.item_end[i] = items;
+    r.a[i] = a;
+    own = own || a.own_k != nullptr;
+    if (a.splits > 1) {
+      const int rows = a.nq * a.num_heads;
+      blocks += (rows * 16 + 255) / 256;
+      m.end_block[n_merge] = blocks;
+      m.rows[n_merge] = rows;
+      m.splits[n_merge] = a.splits;
+      m.part_o[n_merge] = a.part_o;
+      m.part_ml[n_merge] = a.part_ml;
+      m.out[n_merge] = a.out;
+      ++n_merge;
+    }
+  }
+  for (int i = n; i < NB; ++i) {
+    r.item_end[i] = items;
+    r.n_qtiles[i] = 1;
+  }
+  for (int i = n_merge; i < NB; ++i) m.end_block[i] = blocks;
+  r.n_items = items;
+  const int grid = (items + 7) / 8 * 8;
+  if (own)
+    hipLaunchKernelGGL((attn_kernel<true, NB>), dim3(grid), dim3(kThreads), 0, stream, r);
+  else
+    hipLaunchKernelGGL((attn_kernel<false, NB>), dim3(grid), dim3(kThreads), 0, stream, r);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || n_merge == 0) return err;
+  hipLaunchKernelGGL((merge_batch_kernel<NB>), dim3(blocks), dim3(256), 0, stream, m);
   return hipGetLastError();
 }
 

@@ -78,4 +78,10 @@ struct AttnArgs {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 
+// Several runs (independent streams, each with its own pool, row map and
+// partials) in one attention launch and at most one merge launch.  Runs are
+// validated by the caller; n <= kMaxBatchRuns.
+constexpr int kMaxBatchRuns = 16;
+hipError_t launch_attention_batch(const AttnArgs* runs, int n, hipStream_t stream);
+
 }  // namespace spkv

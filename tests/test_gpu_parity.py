@@ -562,3 +562,105 @@ def test_random_schedules_every_frame(seed):
             assert tuple(o.get_cache_stats(b)) == cache.get_cache_stats(b), (seed, f, b)
             assert np.array_equal(synth.bf16_bits(cache.pools[b]), o.pools[b]), (seed, f, b)
     cache.close()
+
+
+# ------------------------------------------------- several streams per launch
+def batch_streams_parity(wls, frames, splits=None, rows=None):
+    """Streams of different shapes advanced together; every frame, one
+    run_batch call runs block 0 of every stream: a run() request on a
+    keyframe (appended, evicted, planned) and a run_own() request on a
+    non-keyframe (the committed cache plus the frame's own K/V).  Each output
+    is checked against the oracle's definition of that request."""
+    need_gpu()
+    import streaming_paged_kv_amd as spkv
+    from oracle.attention import paged_attention_with_own
+    caches = [new_cache(w) for w in wls]
+    for c, sp in zip(caches, splits or [0] * len(wls)):
+        if sp:
+            c.set_num_splits(sp)
+    cfgs = [OracleConfig(**w.cfg_kwargs()) for w in wls]
+    oracles = [PagePoolOracle(cfg, track_pool=[0]) for cfg in cfgs]
+    bits = synth.bf16_bits
+    for f in range(frames):
+        reqs, refs = [], []
+        for w, c, o, cfg in zip(wls, caches, oracles, cfgs):
+            q, k, v = synth.frame_qkv(w, f, 0, device=DEV)
+            S, W = w.scale_frames, w.sliding_window
+            sm = w.head_dim ** -0.5
+            if synth.is_keyframe(w, f):
+                c.append_frame(0, k, v)
+                c.evict_frames(0, S, W)
+                c.plan()
+                o.append_frame(0, bits(k), bits(v))
+                o.evict_frames(0, S, W)
+                pl = o.plan()
+                reqs.append(dict(cache=c, block=0, q=q))
+                refs.append(paged_attention(o.pools[0], pl, cfg, bits(q), sm, rows=rows))
+            else:
+                c.plan()
+                pl = o.plan()
+                reqs.append(dict(cache=c, block=0, q=q, k=k, v=v))
+                refs.append(paged_attention_with_own(o.pools[0], pl, cfg, bits(q), bits(k),
+                                                     bits(v), sm, rows=rows))
+        outs = spkv.run_batch(reqs)
+        torch.cuda.synchronize()
+        for i, (out, ref) in enumerate(zip(outs, refs)):
+            H.compare(out if rows is None else out[rows], ref, ("batch", wls[i].name, f))
+    for c in caches:
+        c.close()
+
+
+def test_run_batch_streams_of_different_shapes():
+    """Three streams in one launch: 4 heads x 16-token pages (22 queries),
+    16 heads x 203-token pages (206 queries), 16 heads x 999-token pages
+    (1005 queries, two query tiles); keyframe intervals 3, 2, 2, so the
+    batches mix run() and run_own() requests."""
+    tiny = synth.WORKLOADS["tiny"].with_(keyframe_interval=3, seed=31)
+    mid = MID.with_(num_blocks=1, seed=32)
+    big = BIGQ.with_(seed=33)
+    log("run_batch: tiny + mid + 1005-query streams, 9 frames")
+    batch_streams_parity([tiny, mid, big], 9)
+
+
+def test_run_batch_sixteen_streams_and_forced_splits():
+    """The largest batch (16 tiny streams: one work item each, no merge), then
+    mid streams with forced split counts 1, 3 and 7 in one batch (one merge
+    launch over requests with different split counts)."""
+    tiny = synth.WORKLOADS["tiny"]
+    wls = [tiny.with_(name=f"tiny{i}", seed=40 + i, keyframe_interval=1 + i % 3)
+           for i in range(16)]
+    log("run_batch: 16 tiny streams, 7 frames")
+    batch_streams_parity(wls, 7)
+    mids = [MID.with_(name=f"mid{i}", num_blocks=1, seed=60 + i) for i in range(3)]
+    log("run_batch: mid streams with splits 1/3/7, 10 frames")
+    batch_streams_parity(mids, 10, splits=[1, 3, 7])
+
+
+def test_run_batch_rejects_overlapping_requests():
+    """A request whose out overlaps another request's q is refused before
+    anything is enqueued: both outputs keep their sentinel bytes."""
+    need_gpu()
+    import streaming_paged_kv_amd as spkv
+    wl = synth.WORKLOADS["tiny"]
+    a, b = new_cache(wl.with_(num_blocks=1)), new_cache(wl.with_(num_blocks=1))
+    for c in (a, b):
+        q, k, v = synth.frame_qkv(wl, 0, 0, device=DEV)
+        c.append_frame(0, k, v)
+        c.evict_frames(0, wl.scale_frames, wl.sliding_window)
+        c.plan()
+    qa = synth.frame_qkv(wl, 1, 0, device=DEV, which=(synth.TENSOR_Q,))[0]
+    oa = torch.full_like(qa, 7.0)
+    shared = torch.full_like(qa, 7.0)          # b's out is a's q
+    with pytest.raises(spkv.SpkvError) as e:
+        spkv.run_batch([dict(cache=a, block=0, q=shared, out=oa),
+                        dict(cache=b, block=0, q=qa, out=shared)])
+    assert e.value.name == "INVALID_ARG"
+    torch.cuda.synchronize()
+    assert bool((oa == 7.0).all()) and bool((shared == 7.0).all())
+    # the same two requests with separate buffers run
+    spkv.run_batch([dict(cache=a, block=0, q=qa, out=oa),
+                    dict(cache=b, block=0, q=qa.clone())])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(oa.float()).all())
+    a.close()
+    b.close()

@@ -184,3 +184,50 @@ def test_run_accepts_several_frames_of_queries():
     for nq in (0, (1 << 20) + 1):
         assert code_of(lambda: c.run(0, nq=nq)) == "INVALID_ARG", nq
     c.close()
+
+
+def test_run_batch_checks_every_request_first():
+    """run_batch (several streams in one launch) applies run()'s checks to
+    every request before anything is enqueued: the first failing request's
+    code comes back, and host-only handles report UNSUPPORTED only once all
+    requests pass."""
+    cfg = CFGS[0]
+    caches = [spkv.PagedKVCache(host_only=True, **cfg) for _ in range(3)]
+    oracles = [PagePoolOracle(OracleConfig(**cfg)) for _ in range(3)]
+    req = lambda i, **kw: dict(cache=caches[i], block=kw.pop("block", 0), **kw)
+    batch = lambda *rs: code_of(lambda: spkv.run_batch(list(rs)))
+    # nothing planned yet: the first request's NOT_PLANNED
+    assert batch(req(0), req(1)) == "NOT_PLANNED"
+    for o, c in zip(oracles, caches):
+        for _ in range(3):
+            o.append_frame(0); c.append_frame(0)
+            o.evict_frames(0, cfg["scale_frames"], cfg["sliding_window"])
+            c.evict_frames(0, cfg["scale_frames"], cfg["sliding_window"])
+    oracles[0].plan(); caches[0].plan()
+    oracles[2].plan(); caches[2].plan()
+    assert batch(req(0), req(1)) == "NOT_PLANNED"        # request 1 unplanned
+    oracles[1].plan(); caches[1].plan()
+    assert batch(req(0), req(1), req(2)) == "UNSUPPORTED"  # every check passed
+    assert batch(req(0), req(2, nq=44)) == "UNSUPPORTED"
+    assert batch(req(1, block=2), req(0)) == "BAD_BLOCK"
+    assert batch(req(0), req(1, nq=0)) == "INVALID_ARG"
+    assert batch(req(0), req(1, sm_scale=float("nan"))) == "INVALID_ARG"
+    assert batch(req(0), req(0)) == "INVALID_ARG"          # a handle twice
+    assert code_of(lambda: spkv.run_batch([req(0)] * 0)) != "OK"
+    many = [spkv.PagedKVCache(host_only=True, **cfg) for _ in range(spkv.MAX_BATCH + 1)]
+    for c in many:
+        c.append_frame(0); c.plan()
+    assert code_of(lambda: spkv.run_batch(
+        [dict(cache=c, block=0) for c in many[:spkv.MAX_BATCH]])) == "UNSUPPORTED"
+    assert code_of(lambda: spkv.run_batch(
+        [dict(cache=c, block=0) for c in many])) == "INVALID_ARG"
+    # STALE_PLAN: block 1 of stream 2 changes after its plan
+    caches[2].append_frame(1)
+    oracles[2].append_frame(1)
+    assert code_of(oracles[2].check_run, 1) == "STALE_PLAN"
+    assert batch(req(0), req(2, block=1)) == "STALE_PLAN"
+    # the state of every handle is what the oracle holds
+    for o, c in zip(oracles, caches):
+        assert_same(o, c)
+    for c in caches + many:
+        c.close()
