@@ -250,12 +250,13 @@ def multi_stream(args, wl, R):
                     else:
                         reqs.append(dict(cache=c, block=b, q=q, k=k, v=v, out=outs[r][b],
                                          sm_scale=sm))
+                batch = spkv.Batch(reqs) if mode == "batched" else None
                 if events:
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record(stream)
                 if mode == "batched":
-                    spkv.run_batch(reqs, stream=stream)
+                    batch.launch(stream=stream)
                 else:
                     for rq in reqs:
                         c = rq["cache"]

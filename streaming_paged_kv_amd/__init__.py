@@ -359,43 +359,56 @@ class PagedKVCache:
         return list(sc[:ns.value]), list(lv[:nl.value]), list(fr[:nf.value]), nsf.value
 
 
-def run_batch(requests, stream=None):
-    """Several streams' runs in one launch (spkv_run_batch).
+class Batch:
+    """The marshalled requests of one spkv_run_batch call; launch() makes it.
 
     requests: sequence of dicts with keys cache (a PagedKVCache), block, q and
     optionally out, k and v (the caller's own frame, as for run_own), sm_scale
-    and nq.  Host-only caches pass no tensors.  Returns the outputs, in order
-    (None for host-only caches).
+    and nq.  Host-only caches pass no tensors.  outs holds the output tensors,
+    in order (None for host-only caches).
     """
-    requests = list(requests)
-    lib = load_library()
-    arr = (Request * max(1, len(requests)))()
-    outs = []
-    host_only = not requests or requests[0]["cache"].host_only
-    for i, r in enumerate(requests):
-        c = r["cache"]
-        sm = r.get("sm_scale")
-        if sm is None:
-            sm = c.cfg["head_dim"] ** -0.5
-        arr[i].handle = c._h
-        arr[i].block = r["block"]
-        arr[i].sm_scale = float(sm)
-        if c.host_only:
-            arr[i].nq = c.tokens_per_frame if r.get("nq") is None else r["nq"]
-            outs.append(None)
-            continue
-        q = r["q"]
-        n = q.shape[0] if r.get("nq") is None else r["nq"]
-        arr[i].nq = n
-        arr[i].q = c._frame_tensor(q, "q", n)
-        out = r.get("out")
-        if out is None:
-            out = torch.empty_like(q)
-        arr[i].out = c._frame_tensor(out, "out", n)
-        if r.get("k") is not None or r.get("v") is not None:
-            arr[i].own_k = c._frame_tensor(r.get("k"), "k", c.tokens_per_frame)
-            arr[i].own_v = c._frame_tensor(r.get("v"), "v", c.tokens_per_frame)
-        outs.append(out)
-    s = None if host_only else _stream_ptr(stream)
-    _check(lib.spkv_run_batch(arr, len(requests), s), "spkv_run_batch")
-    return outs
+
+    def __init__(self, requests):
+        requests = list(requests)
+        self.lib = load_library()
+        self.n = len(requests)
+        self.arr = (Request * max(1, self.n))()
+        self.outs = []
+        self.host_only = not requests or requests[0]["cache"].host_only
+        self._keep = requests
+        for i, r in enumerate(requests):
+            c = r["cache"]
+            sm = r.get("sm_scale")
+            if sm is None:
+                sm = c.cfg["head_dim"] ** -0.5
+            a = self.arr[i]
+            a.handle = c._h
+            a.block = r["block"]
+            a.sm_scale = float(sm)
+            if c.host_only:
+                a.nq = c.tokens_per_frame if r.get("nq") is None else r["nq"]
+                self.outs.append(None)
+                continue
+            q = r["q"]
+            n = q.shape[0] if r.get("nq") is None else r["nq"]
+            a.nq = n
+            a.q = c._frame_tensor(q, "q", n)
+            out = r.get("out")
+            if out is None:
+                out = torch.empty_like(q)
+            a.out = c._frame_tensor(out, "out", n)
+            if r.get("k") is not None or r.get("v") is not None:
+                a.own_k = c._frame_tensor(r.get("k"), "k", c.tokens_per_frame)
+                a.own_v = c._frame_tensor(r.get("v"), "v", c.tokens_per_frame)
+            self.outs.append(out)
+
+    def launch(self, stream=None):
+        s = None if self.host_only else _stream_ptr(stream)
+        _check(self.lib.spkv_run_batch(self.arr, self.n, s), "spkv_run_batch")
+        return self.outs
+
+
+def run_batch(requests, stream=None):
+    """Several streams' runs in one launch (spkv_run_batch); see Batch.
+    Returns the outputs, in order (None for host-only caches)."""
+    return Batch(requests).launch(stream)
