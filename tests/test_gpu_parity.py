@@ -664,3 +664,94 @@ def test_run_batch_rejects_overlapping_requests():
     assert bool(torch.isfinite(oa.float()).all())
     a.close()
     b.close()
+
+
+@pytest.mark.parametrize("seed", [201, 202])
+def test_run_batch_random_schedules(seed):
+    """Three streams of different geometry, each with its own seeded random
+    mix of keyframes, transient non-keyframes, run_own non-keyframes,
+    deferred accept / reject and resets; per frame and block one run_batch
+    covers the three streams.  After every frame each stream's whole pool,
+    stats and allocator state are bit-exact and every output matches the
+    oracle."""
+    need_gpu()
+    import streaming_paged_kv_amd as spkv
+    from oracle.attention import paged_attention_with_own
+    rng = np.random.default_rng(seed)
+    wls = [synth.WORKLOADS["tiny"].with_(num_blocks=2, frames=30, seed=seed),
+           synth.Workload("odd", 2, 2, 64, 13, 11, 4, 1, 3, 1, 40, 30, seed=seed + 1),
+           MID.with_(name="mid2", frames=30, seed=seed + 2)]
+    nb = 2
+    cfgs = [OracleConfig(**w.cfg_kwargs()) for w in wls]
+    oracles = [PagePoolOracle(cfg, track_pool=range(nb)) for cfg in cfgs]
+    caches = [new_cache(w) for w in wls]
+    for c in caches:
+        c.set_num_splits(int(rng.integers(0, 4)))
+    committed = [0] * len(wls)
+    limits = [30, 36, 60]                  # stay clear of special-slot overflow
+    for f in range(30):
+        evs = []
+        for i, (c, o) in enumerate(zip(caches, oracles)):
+            ev = str(rng.choice(["key", "key", "transient", "own", "accept", "reject", "reset"]))
+            if ev == "reset" or committed[i] >= limits[i]:
+                c.reset()
+                o.reset()
+                committed[i] = 0
+                ev = "key"
+            if committed[i] == 0 and ev == "own":
+                ev = "key"
+            evs.append(ev)
+        qkvs = [H.gen_frame(w, f, nb, DEV) for w in wls]
+        bits = [[[synth.bf16_bits(t) for t in x] for x in qkv] for qkv in qkvs]
+        for i, ev in enumerate(evs):
+            if ev in ("transient", "accept", "reject"):
+                caches[i].set_defer_eviction(True)
+                oracles[i].set_defer_eviction(True)
+        for b in range(nb):
+            reqs, refs = [], []
+            for i, (w, c, o, cfg, ev) in enumerate(zip(wls, caches, oracles, cfgs, evs)):
+                q, k, v = qkvs[i][b]
+                qb, kb, vb = bits[i][b]
+                S, W = w.scale_frames, w.sliding_window
+                sm = w.head_dim ** -0.5
+                if ev == "own":
+                    if b == 0:
+                        c.plan()
+                        o.plan()
+                    reqs.append(dict(cache=c, block=b, q=q, k=k, v=v))
+                    refs.append(paged_attention_with_own(o.pools[b], o.check_run(b), cfg,
+                                                         qb, kb, vb, sm))
+                else:
+                    c.append_frame(b, k, v)
+                    o.append_frame(b, kb, vb)
+                    c.evict_frames(b, S, W)
+                    o.evict_frames(b, S, W)
+                    if b == 0:
+                        c.plan()
+                        o.plan()
+                    reqs.append(dict(cache=c, block=b, q=q))
+                    refs.append(paged_attention(o.pools[b], o.check_run(b), cfg, qb, sm))
+            outs = spkv.run_batch(reqs)
+            torch.cuda.synchronize()
+            for i, (out, ref) in enumerate(zip(outs, refs)):
+                H.compare(out, ref, ("batch random", seed, f, wls[i].name, evs[i], b))
+        for i, (w, c, o, ev) in enumerate(zip(wls, caches, oracles, evs)):
+            for b in range(nb):
+                if ev in ("transient", "reject"):
+                    c.rollback_last_frame(b)
+                    o.rollback_last_frame(b)
+                elif ev == "accept":
+                    c.execute_deferred_eviction(b, w.scale_frames, w.sliding_window)
+                    o.execute_deferred_eviction(b, w.scale_frames, w.sliding_window)
+            if ev in ("transient", "accept", "reject"):
+                c.set_defer_eviction(False)
+                o.set_defer_eviction(False)
+            committed[i] += ev in ("key", "accept")
+        torch.cuda.synchronize()
+        for i, (c, o) in enumerate(zip(caches, oracles)):
+            for b in range(nb):
+                assert list(o.block_state(b)) == list(c.get_block_state(b)), (seed, f, i, b)
+                assert tuple(o.get_cache_stats(b)) == c.get_cache_stats(b), (seed, f, i, b)
+                assert np.array_equal(synth.bf16_bits(c.pools[b]), o.pools[b]), (seed, f, i, b)
+    for c in caches:
+        c.close()
