@@ -253,8 +253,9 @@ typedef struct {
  * or none; no request's out may overlap another request's q, out, own_k or
  * own_v.  The key ranges are split so that the work items of all requests
  * are about equally long and fill the CUs once.  Nothing is enqueued unless
- * every request passes its checks: the first failing request's code is
- * returned (host-only handles: UNSUPPORTED after the checks).  Enqueues one
+ * every check passes: first the checks across requests (INVALID_ARG), then
+ * run()'s checks request by request, the first failure's code being
+ * returned (host-only handles: UNSUPPORTED once all pass).  Enqueues one
  * attention kernel and, if any range is split, one merge kernel. */
 SPKV_API int spkv_run_batch(const spkv_request* reqs, int32_t n, void* hip_stream);
 
