@@ -174,6 +174,43 @@ def test_edge_cases_nq_scale_and_sharp_keys():
     cache.close()
 
 
+def test_maximum_query_rows():
+    """The largest query count run() takes (2^20 rows, 2048 query tiles x 4
+    heads = 8192 work items) over a tiny stream's 12 frames: sampled rows
+    (first, last, tile edges, random) against the oracle, at the automatic
+    split and at a forced split of 3 (2^20 x 4 x 64 fp32 partials)."""
+    need_gpu()
+    wl = synth.WORKLOADS["tiny"]
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    o = PagePoolOracle(cfg, track_pool=[0])
+    import streaming_paged_kv_amd as spkv
+    nq = 1 << 20
+    # workspace for 3 splits of 2^20 rows: partial O + (m, l)
+    ws = spkv.query_sizes(**wl.cfg_kwargs())[2] + 3 * nq * wl.num_heads * (64 + 2) * 4 + 4096
+    cache = new_cache(wl, workspace_bytes=ws)
+    for f in range(wl.frames):
+        q, k, v = synth.frame_qkv(wl, f, 0, device=DEV)
+        cache.append_frame(0, k, v)
+        cache.evict_frames(0, wl.scale_frames, wl.sliding_window)
+        o.append_frame(0, synth.bf16_bits(k), synth.bf16_bits(v))
+        o.evict_frames(0, wl.scale_frames, wl.sliding_window)
+    cache.plan()
+    pl = o.plan()
+    gen = torch.Generator(device=DEV).manual_seed(77)
+    q = torch.randn((nq, wl.num_heads, wl.head_dim), generator=gen,
+                    device=DEV).to(torch.bfloat16)
+    rows = H.sample_rows(nq, extra=48, seed=5) + [nq - 512, nq - 513, (nq >> 1) + 17]
+    rows = sorted(set(rows))
+    qb = synth.bf16_bits(q[rows])
+    ref = paged_attention(o.pools[0], pl, cfg, qb, wl.head_dim ** -0.5)
+    for splits in (0, 3):
+        cache.set_num_splits(splits)
+        out = cache.run(0, q)
+        torch.cuda.synchronize()
+        H.compare(out[rows], ref, ("max nq", splits))
+    cache.close()
+
+
 @pytest.mark.parametrize("mode", ["all_far_below", "all_far_above", "mixed"])
 def test_extreme_logits(mode):
     """Scores far from 0: every score of a frame about -50 (every p would
