@@ -1,0 +1,98 @@
+/* A plain C99 client of include/spkv.h (no C++, no Python): drives a
+ * host-only handle through the append -> evict -> plan steps of a stream and
+ * prints, per frame, the plan, the free list and the stats, then the codes
+ * of a few calls whose result the contract fixes.  tests/test_c_client.py
+ * builds it with gcc, runs it and checks the output.
+ *
+ * usage: c_abi_client NB H D PS P NS S W R MTF FRAMES */
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "spkv.h"
+
+#define CAP 4096
+
+static void print_list(const char* tag, const int32_t* v, int32_t n) {
+  int32_t i;
+  printf(" %s", tag);
+  for (i = 0; i < n; ++i) printf(" %d", (int)v[i]);
+}
+
+int main(int argc, char** argv) {
+  spkv_config c;
+  spkv_handle* h = NULL;
+  spkv_handle* h2 = NULL;
+  static int32_t table[CAP], scale[CAP], live[CAP], free_list[CAP];
+  int32_t n_pages, n_patch, lpl, n_scale, n_live, n_free;
+  int64_t nsf;
+  spkv_stats st;
+  spkv_request req[2];
+  int frames, f, rc;
+  if (argc != 12) {
+    fprintf(stderr, "usage: %s NB H D PS P NS S W R MTF FRAMES\n", argv[0]);
+    return 2;
+  }
+  c.num_blocks = atoi(argv[1]);
+  c.num_heads = atoi(argv[2]);
+  c.head_dim = atoi(argv[3]);
+  c.page_size = atoi(argv[4]);
+  c.patch_tokens = atoi(argv[5]);
+  c.num_special_tokens = atoi(argv[6]);
+  c.scale_frames = atoi(argv[7]);
+  c.sliding_window = atoi(argv[8]);
+  c.headroom = atoi(argv[9]);
+  c.max_total_frames = atoi(argv[10]);
+  frames = atoi(argv[11]);
+
+  rc = spkv_create(&c, NULL, NULL, 0, &h);
+  printf("create %d\n", rc);
+  if (rc != SPKV_OK) return 1;
+  printf("run_before_plan %d\n", spkv_run(h, 0, NULL, NULL, 1, 0.125f, NULL));
+  printf("plan_empty %d\n", spkv_plan(h, NULL));
+  for (f = 0; f < frames; ++f) {
+    if (spkv_append_frame(h, 0, NULL, NULL, NULL) != SPKV_OK ||
+        spkv_evict_frames(h, 0, c.scale_frames, c.sliding_window, 1, 0) != SPKV_OK ||
+        spkv_plan(h, NULL) != SPKV_OK ||
+        spkv_get_plan(h, table, CAP, &n_pages, &n_patch, &lpl) != SPKV_OK ||
+        spkv_get_block_state(h, 0, scale, live, free_list, CAP, &n_scale, &n_live,
+                             &n_free, &nsf) != SPKV_OK ||
+        spkv_get_cache_stats(h, 0, &st) != SPKV_OK) {
+      printf("frame %d failed\n", f);
+      return 1;
+    }
+    printf("frame %d", f);
+    print_list("table", table, n_pages);
+    printf(" lpl %d", (int)lpl);
+    print_list("free", free_list, n_free);
+    printf(" stats %lld %d %d %d %lld\n", (long long)st.frame_count, (int)st.scale_pages,
+           (int)st.live_pages, (int)st.free_pages, (long long)st.special_tokens);
+  }
+  /* checks pass on a host-only handle, then UNSUPPORTED */
+  printf("run %d\n", spkv_run(h, 0, NULL, NULL, c.num_special_tokens + c.patch_tokens,
+                              0.125f, NULL));
+  printf("bad_block %d\n", spkv_run(h, c.num_blocks, NULL, NULL, 1, 0.125f, NULL));
+  rc = spkv_create(&c, NULL, NULL, 0, &h2);
+  if (rc != SPKV_OK || spkv_append_frame(h2, 0, NULL, NULL, NULL) != SPKV_OK ||
+      spkv_plan(h2, NULL) != SPKV_OK)
+    return 1;
+  req[0].handle = h;
+  req[0].block = 0;
+  req[0].nq = c.num_special_tokens + c.patch_tokens;
+  req[0].q = NULL;
+  req[0].out = NULL;
+  req[0].own_k = NULL;
+  req[0].own_v = NULL;
+  req[0].sm_scale = 0.125f;
+  req[1] = req[0];
+  req[1].handle = h2;
+  printf("run_batch %d\n", spkv_run_batch(req, 2, NULL));
+  req[1].handle = h;
+  printf("run_batch_same_handle %d\n", spkv_run_batch(req, 2, NULL));
+  printf("run_batch_empty %d\n", spkv_run_batch(req, 0, NULL));
+  printf("rollback_after_evictions %d\n", spkv_rollback_last_frame(h, 0));
+  printf("reset %d\n", spkv_reset(h));
+  printf("run_after_reset %d\n", spkv_run(h, 0, NULL, NULL, 1, 0.125f, NULL));
+  printf("destroy %d %d\n", spkv_destroy(h), spkv_destroy(h2));
+  printf("error_string %s\n", spkv_error_string(SPKV_ERR_STALE_PLAN));
+  return 0;
+}
