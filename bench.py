@@ -92,6 +92,8 @@ def cpu_baseline(wl, warm_frames, n_blocks_timed):
 
     def one_frame(f, kind, attend_blocks):
         kv = frames[f % 4]
+        if o.get_cache_stats(0)[0] >= cfg.special_capacity_frames:
+            o.reset()   # special stream full (short streams): start over
         if wl.dynamic or kind == "transient":
             o.set_defer_eviction(True)
         for b in range(wl.num_blocks):
@@ -376,6 +378,8 @@ def main():
     sm = wl.head_dim ** -0.5
     hd = wl.num_heads * wl.head_dim
     nq = wl.tokens_per_frame
+    fpp = wl.page_size // wl.num_special_tokens
+    special_cap = -(-wl.max_total_frames // fpp) * fpp   # frames the special pages hold
 
     # Three windows over consecutive frames of the same stream:
     #   A  the timed region (value, ms_per_step): no events at all, since each
@@ -415,6 +419,12 @@ def main():
             return
         if wl.dynamic:
             cache.set_defer_eviction(True)
+        if cache.get_cache_stats(0)[0] >= special_cap:
+            # The special stream is full (only short streams get there within
+            # the run): start over, as a streaming system resets its cache.
+            cache.reset()
+            if wl.dynamic:
+                cache.set_defer_eviction(True)
         nk = None
         if mode == "C":
             # The frame's appends of all blocks back to back between two
