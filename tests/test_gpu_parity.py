@@ -211,6 +211,75 @@ def test_maximum_query_rows():
     cache.close()
 
 
+# 4094 patch pages + 2 special pages of 1 MiB (256 tokens x 16 heads x 64 dims,
+# K and V): a pool of exactly 4 GiB, whose special pages lie at the top of
+# the range that 32-bit byte offsets address.
+POOL_4GIB = synth.Workload("pool-4GiB", 1, 16, 64, 256, 256, 6, 2, 4090, 2, 84, 44, seed=31)
+
+
+def test_pool_offsets_up_to_4gib_and_pool_size_limits():
+    """run() on a 4 GiB pool: the special pages sit at byte offsets 4094 MiB
+    and 4095 MiB (the second from frame 42 on, 42 frames per special page),
+    so the kernel's loads use offsets above 2^31 up to the top of the 32-bit
+    range.  Attention and the visible pages' bytes against the oracle at
+    chosen frames.  run_own() on that pool is UNSUPPORTED (its row map marks
+    the caller's rows with the offsets' top bit), and run() on a pool one
+    page over 4 GiB is UNSUPPORTED, with nothing enqueued."""
+    need_gpu()
+    import streaming_paged_kv_amd as spkv
+    wl = POOL_4GIB
+    assert spkv.query_sizes(**wl.cfg_kwargs())[1] == 1 << 32
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    o = PagePoolOracle(cfg, track_pool=[0])
+    cache = new_cache(wl)
+    S, W = wl.scale_frames, wl.sliding_window
+    sm = wl.head_dim ** -0.5
+    checked = 0
+    for f in range(wl.frames):
+        q, k, v = synth.frame_qkv(wl, f, 0, device=DEV)
+        cache.append_frame(0, k, v)
+        cache.evict_frames(0, S, W)
+        cache.plan()
+        out = cache.run(0, q)
+        o.append_frame(0, synth.bf16_bits(k), synth.bf16_bits(v))
+        o.evict_frames(0, S, W)
+        pl = o.plan()
+        if f not in (0, 1, 5, 41, 42, 43):
+            continue
+        torch.cuda.synchronize()
+        table = list(o.plan_state.table)
+        assert cache.get_plan()[0] == table, f
+        assert table[-1] == 4094 + f // 42, f
+        ref = paged_attention(o.pools[0], pl, cfg, synth.bf16_bits(q), sm)
+        H.compare(out, ref, ("4 GiB pool", f))
+        for page in table:
+            assert np.array_equal(synth.bf16_bits(cache.pools[0][page]), o.pools[0][page]), (f, page)
+        checked += 1
+        log(f"  4 GiB pool frame {f}: table ends at page {table[-1]}")
+    assert checked == 6
+    q, k, v = synth.frame_qkv(wl, wl.frames, 0, device=DEV)
+    with pytest.raises(spkv.SpkvError) as ei:
+        cache.run_own(0, q, k, v)
+    assert ei.value.name == "UNSUPPORTED"
+    cache.close()
+    del cache
+    torch.cuda.empty_cache()
+
+    over = wl.with_(name="pool-4GiB+1MiB", sliding_window=4091, frames=1)
+    assert spkv.query_sizes(**over.cfg_kwargs())[1] == (1 << 32) + (1 << 20)
+    cache = new_cache(over)
+    q, k, v = synth.frame_qkv(over, 0, 0, device=DEV)
+    cache.append_frame(0, k, v)
+    cache.plan()
+    out = torch.full_like(q, 7.0)
+    with pytest.raises(spkv.SpkvError) as ei:
+        cache.run(0, q, out=out)
+    assert ei.value.name == "UNSUPPORTED"
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    cache.close()
+
+
 @pytest.mark.parametrize("mode", ["all_far_below", "all_far_above", "mixed"])
 def test_extreme_logits(mode):
     """Scores far from 0: every score of a frame about -50 (every p would
