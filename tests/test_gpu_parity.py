@@ -526,6 +526,20 @@ def test_run_own_518x378_steady_state():
                rows=H.sample_rows(wl.tokens_per_frame))
 
 
+def test_run_own_pool_offsets_up_to_2gib():
+    """run_own on a pool of exactly 2 GiB (the largest it takes: its row map
+    marks the caller's rows with the top bit of the 32-bit offsets): 2046
+    patch pages and 2 special pages of 1 MiB; from the 43rd keyframe on the
+    cache's special rows sit in the last MiB below 2^31, next to the caller's
+    marked rows in the same row map."""
+    wl = synth.Workload("pool-2GiB", 1, 16, 64, 256, 256, 6, 2, 2042, 2, 84, 88,
+                        keyframe_interval=2, seed=32)
+    import streaming_paged_kv_amd as spkv
+    assert spkv.query_sizes(**wl.cfg_kwargs())[1] == 1 << 31
+    log("run_own, 2 GiB pool")
+    own_parity(wl, check_frames={1, 3, 85, 87})
+
+
 def test_run_own_rejects_overlap_and_missing_buffers():
     need_gpu()
     import streaming_paged_kv_amd as spkv
