@@ -114,6 +114,29 @@ def test_mid_stream_ragged_pages_and_splits(splits):
     full_parity(MID, splits=splits)
 
 
+DEGENERATE = synth.Workload("degenerate", 2, 3, 64, 6, 5, 6, 0, 1, 1, 30, 30, seed=41)
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_degenerate_geometry(splits):
+    """No scale frames, a one-page window with one page of headroom, 6-token
+    pages (one frame per special page, so a 64-key tile spans 11 pages),
+    5 patch tokens in 6-token pages, 3 heads, and the special stream filled
+    to its last slot (30 frames, 30 special pages)."""
+    log(f"degenerate geometry, splits={splits}")
+    full_parity(DEGENERATE, splits=splits)
+    cache = new_cache(DEGENERATE)
+    import streaming_paged_kv_amd as spkv
+    for f in range(DEGENERATE.frames):
+        _, k, v = synth.frame_qkv(DEGENERATE, f, 0, device=DEV)
+        cache.append_frame(0, k, v)
+        cache.evict_frames(0, 0, 1)
+    with pytest.raises(spkv.SpkvError) as ei:
+        cache.append_frame(0, k, v)
+    assert ei.value.name == "SPECIAL_OVERFLOW"
+    cache.close()
+
+
 BIGQ = synth.Workload("bigq", 1, 16, 64, 999, 999, 6, 1, 2, 1, 400, 6,
                       keyframe_interval=2, k_scale=0.5, seed=22)
 
