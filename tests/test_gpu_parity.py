@@ -137,6 +137,14 @@ def test_degenerate_geometry(splits):
     cache.close()
 
 
+def test_many_heads():
+    """80 heads: 10 KiB token rows in the pool, 80 work items per query tile
+    and split, head slices past the first 8 KiB of a row."""
+    wl = synth.Workload("80-heads", 1, 80, 64, 64, 58, 6, 1, 3, 1, 40, 8, seed=42)
+    log("80 heads")
+    full_parity(wl)
+
+
 BIGQ = synth.Workload("bigq", 1, 16, 64, 999, 999, 6, 1, 2, 1, 400, 6,
                       keyframe_interval=2, k_scale=0.5, seed=22)
 
