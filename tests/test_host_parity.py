@@ -231,3 +231,35 @@ def test_run_batch_checks_every_request_first():
         assert_same(o, c)
     for c in caches + many:
         c.close()
+
+
+def test_separate_handles_from_concurrent_threads():
+    """Handles share no state: eight threads, each driving its own host-only
+    handle (the C calls run without the interpreter lock) through a seeded
+    random operation sequence, each checked step by step against its own
+    oracle."""
+    import random
+    import threading
+    ops = ["append", "append", "append", "evict", "evict", "defer", "execute",
+           "rollback", "plan", "plan", "run", "run_own", "reset", "evict_badS",
+           "evict_flags"]
+    errors = []
+
+    def worker(t):
+        rng = random.Random(1000 + t)
+        o, c = make_pair(**CFGS[t % len(CFGS)])
+        try:
+            for _ in range(400):
+                step(o, c, rng.choice(ops), rng.randint(-1, 3), rng.randint(0, 6))
+                assert_same(o, c)
+        except Exception as e:      # reported by the main thread
+            errors.append((t, repr(e)))
+        finally:
+            c.close()
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
