@@ -906,3 +906,50 @@ def test_run_batch_random_schedules(seed):
                 assert np.array_equal(synth.bf16_bits(c.pools[b]), o.pools[b]), (seed, f, i, b)
     for c in caches:
         c.close()
+
+
+def test_two_handles_on_concurrent_streams():
+    """Two handles, each on its own HIP stream (default priority), with their
+    frame steps interleaved and no synchronisation between the streams:
+    every output equals, bit for bit, the same frames run one handle after
+    the other on one stream.  Handles share nothing on the device (own pools
+    and workspaces) or on the host (own staging)."""
+    need_gpu()
+    wls = [MID.with_(name="conc-a", num_blocks=2, frames=10, seed=51),
+           BIGQ.with_(name="conc-b", frames=6, seed=52)]
+    inputs = [[H.gen_frame(wl, f, wl.num_blocks, DEV) for f in range(wl.frames)] for wl in wls]
+
+    def drive(cache, wl, f, outs, stream):
+        for b in range(wl.num_blocks):
+            q, k, v = inputs[wls.index(wl)][f][b]
+            cache.append_frame(b, k, v, stream=stream)
+            cache.evict_frames(b, wl.scale_frames, wl.sliding_window)
+            if b == 0:
+                cache.plan(stream=stream)
+            cache.run(b, q, out=outs[b], stream=stream)
+
+    # concurrent: frame steps alternate between the two streams
+    caches = [new_cache(wl) for wl in wls]
+    got = [[[torch.empty_like(x[0]) for x in inputs[i][f]] for f in range(wl.frames)]
+           for i, wl in enumerate(wls)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:              # pools zeroed and inputs drawn on this stream
+        s.wait_stream(torch.cuda.current_stream())
+    for f in range(max(wl.frames for wl in wls)):
+        for i, wl in enumerate(wls):
+            if f < wl.frames:
+                drive(caches[i], wl, f, got[i][f], streams[i])
+    torch.cuda.synchronize()
+    for c in caches:
+        c.close()
+
+    # reference: one handle after the other on the default stream
+    for i, wl in enumerate(wls):
+        cache = new_cache(wl)
+        for f in range(wl.frames):
+            outs = [torch.empty_like(x[0]) for x in inputs[i][f]]
+            drive(cache, wl, f, outs, None)
+            torch.cuda.synchronize()
+            for b in range(wl.num_blocks):
+                assert torch.equal(outs[b], got[i][f][b]), (wl.name, f, b)
+        cache.close()
