@@ -203,7 +203,9 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream);
  * live and special state differ from block 0's at plan time.  UNSUPPORTED
  * when a block's pool exceeds 4 GiB (pool rows are addressed by 32-bit byte
  * offsets).  Enqueues the attention kernel (and, when the key range is split,
- * a merge kernel). */
+ * a merge kernel) and nothing else, so a run of a planned frame may be
+ * captured into a HIP graph and replayed; plan() may not, since it copies
+ * the host allocator's state of the moment. */
 SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
                       int32_t nq, float sm_scale, void* hip_stream);
 

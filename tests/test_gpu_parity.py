@@ -953,3 +953,47 @@ def test_two_handles_on_concurrent_streams():
             for b in range(wl.num_blocks):
                 assert torch.equal(outs[b], got[i][f][b]), (wl.name, f, b)
         cache.close()
+
+
+def test_run_captured_in_a_hip_graph():
+    """run() enqueues kernels only (attention, and the merge when the key
+    range is split): captured into a HIP graph after a plan, every replay
+    equals the eager result bit for bit, with eager work and
+    synchronisation between replays.  plan() is not capturable: it reads
+    the host allocator's state of the moment."""
+    need_gpu()
+    wl = BIGQ.with_(name="graph", frames=4, seed=61)
+    cache = new_cache(wl)
+    frames = [H.gen_frame(wl, f, 1, DEV)[0] for f in range(wl.frames)]
+    for f, (q, k, v) in enumerate(frames):
+        cache.append_frame(0, k, v)
+        cache.evict_frames(0, wl.scale_frames, wl.sliding_window)
+        cache.plan()
+        if f < wl.frames - 1:
+            cache.run(0, q)
+    q = frames[-1][0]
+    for splits in (0, 1):
+        cache.set_num_splits(splits)
+        ref = cache.run(0, q)
+        torch.cuda.synchronize()
+        out = torch.empty_like(q)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            cache.run(0, q, out=out)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cache.run(0, q, out=out)
+        for i in range(4):
+            out.fill_(0)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), (splits, i)
+            # eager work of the program between replays
+            junk = torch.randn(1 << 20, device=DEV)
+            assert torch.isfinite(junk.sum())
+            torch.cuda.synchronize()
+        del g
+    cache.close()
