@@ -609,17 +609,10 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
   const int row = gid >> 4;   // (query, head) flattened
   const int d0 = (gid & 15) * 4;
   if (row >= rows) return;
+  // One pass: each group's (m, l) and O are loaded together and folded into
+  // a running reference, so a row costs one memory round trip per group of
+  // splits (one in all launches of up to kMergeGroup splits).
   float mmax = -INFINITY;
-  for (int s0 = 0; s0 < splits; s0 += kMergeGroup) {
-    float mv[kMergeGroup];
-#pragma unroll
-    for (int j = 0; j < kMergeGroup; ++j) {
-      const int sj = min(s0 + j, splits - 1);
-      mv[j] = part_ml[(size_t(sj) * rows + row) * 2];
-    }
-#pragma unroll
-    for (int j = 0; j < kMergeGroup; ++j) mmax = fmaxf(mmax, mv[j]);
-  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float lsum = 0.f;
   for (int s0 = 0; s0 < splits; s0 += kMergeGroup) {
@@ -631,6 +624,18 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
       ml[j] = *reinterpret_cast<const float2*>(part_ml + r * 2);
       ov[j] = *reinterpret_cast<const float4*>(part_o + r * kD + d0);
     }
+    float gmax = mmax;
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) gmax = fmaxf(gmax, ml[j].x);
+    // Every split saw at least one key, so gmax is finite; the first group
+    // scales the empty accumulators by 2^-inf = 0.
+    const float rescale = __builtin_amdgcn_exp2f(mmax - gmax);
+    acc.x *= rescale;
+    acc.y *= rescale;
+    acc.z *= rescale;
+    acc.w *= rescale;
+    lsum *= rescale;
+    mmax = gmax;
 #pragma unroll
     for (int j = 0; j < kMergeGroup; ++j) {
       const float w = s0 + j < splits ? __builtin_amdgcn_exp2f(ml[j].x - mmax) : 0.f;
