@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2,
                     help="blocks of the oracle frame timed (scaled to all)")
+    ap.add_argument("--no-full-stream", action="store_true",
+                    help="skip the timed pass over the whole stream from an empty cache")
     ap.add_argument("--no-events", action="store_true",
                     help="time without per-kernel events (roofline omitted)")
     ap.add_argument("--append-sweep", action="store_true",
@@ -367,7 +369,7 @@ def main():
     n_attn = 0 if args.no_events else args.steps     # window B frames
     n_app = 0 if args.no_events else min(args.steps, 20)  # window C frames
     total = args.warmup + args.steps + n_attn
-    sched = frame_schedule(wl, total + n_app)
+    sched = frame_schedule(wl, max(total + n_app, wl.frames))
 
     # input bank, resident in HBM before timing
     nbank = max(1, min(args.bank, total))
@@ -478,6 +480,21 @@ def main():
             step(f, "C")
         torch.cuda.synchronize()
 
+    # The whole stream as its configuration defines it (frames 0..frames-1)
+    # from an empty cache, no events: the scale pages and the window filling
+    # up are included, so this rate is above the steady-state one.
+    full = None
+    if not args.no_full_stream:
+        cache.reset()
+        torch.cuda.synchronize()
+        t_full = time.perf_counter()
+        for f in range(wl.frames):
+            step(f, None)
+        torch.cuda.synchronize()
+        t_full = time.perf_counter() - t_full
+        full = {"value": wl.frames / t_full, "unit": "frames/s", "frames": wl.frames,
+                "window": f"frames 0..{wl.frames - 1} from an empty cache, no events"}
+
     result = {
         "metric": METRIC,
         "value": args.steps / dt,
@@ -504,6 +521,8 @@ def main():
             "input_bank_frames": nbank,
         },
     }
+    if full is not None:
+        result["full_stream"] = full
     if use_ev:
         t_attn = [a.elapsed_time(b) * 1e-3 for a, b in ev_attn]
         t_app = [a.elapsed_time(b) * 1e-3 for a, b in ev_app]
