@@ -218,7 +218,7 @@ SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
  * append_frame takes).  Neither the pool nor any state changes, so there is
  * nothing to roll back.  Arguments and errors as for run(); own_k and own_v
  * must not overlap out.  UNSUPPORTED when a block's pool exceeds 2 GiB (run()
- * itself takes pools up to 4 GiB).  Host-only handles pass NULL own_k and
+ * itself takes pools up to 4 GiB).  Enqueues kernels only, as run() does.  Host-only handles pass NULL own_k and
  * own_v and get run()'s checks and result. */
 SPKV_API int spkv_run_own(spkv_handle* h, int32_t block, const void* q, void* out,
                           int32_t nq, float sm_scale, const void* own_k,
@@ -258,7 +258,8 @@ typedef struct {
  * every check passes: first the checks across requests (INVALID_ARG), then
  * run()'s checks request by request, the first failure's code being
  * returned (host-only handles: UNSUPPORTED once all pass).  Enqueues one
- * attention kernel and, if any range is split, one merge kernel. */
+ * attention kernel and, if any range is split, one merge kernel, and nothing
+ * else: like run() and run_own(), it may be captured into a HIP graph. */
 SPKV_API int spkv_run_batch(const spkv_request* reqs, int32_t n, void* hip_stream);
 
 /* Split of the key range across workgroups used by run(): 0 = automatic

@@ -997,3 +997,61 @@ def test_run_captured_in_a_hip_graph():
             torch.cuda.synchronize()
         del g
     cache.close()
+
+
+def test_run_own_and_run_batch_captured_in_a_hip_graph():
+    """run_own() and run_batch() enqueue kernels only as well: captured after
+    the streams' plans, their replays equal the eager results bit for bit,
+    with eager work and synchronisation between replays."""
+    need_gpu()
+    import streaming_paged_kv_amd as spkv
+    wls = [BIGQ.with_(name="graph-a", frames=5, seed=62),
+           MID.with_(name="graph-b", num_blocks=1, frames=5, seed=63)]
+    caches = [new_cache(wl) for wl in wls]
+    last = []
+    for wl, cache in zip(wls, caches):
+        frames = [H.gen_frame(wl, f, 1, DEV)[0] for f in range(wl.frames)]
+        for q, k, v in frames[:-1]:
+            cache.append_frame(0, k, v)
+            cache.evict_frames(0, wl.scale_frames, wl.sliding_window)
+            cache.plan()
+        last.append(frames[-1])
+
+    def requests(outs):
+        (qa, ka, va), (qb, _, _) = last
+        return [dict(cache=caches[0], block=0, q=qa, k=ka, v=va, out=outs[0]),
+                dict(cache=caches[1], block=0, q=qb, out=outs[1])]
+
+    cases = {
+        "run_own": lambda outs: caches[0].run_own(0, last[0][0], last[0][1], last[0][2],
+                                                  out=outs[0]),
+        "run_batch": lambda outs: spkv.run_batch(requests(outs)),
+    }
+    for name, call in cases.items():
+        ref = [torch.empty_like(last[0][0]), torch.empty_like(last[1][0])]
+        call(ref)
+        torch.cuda.synchronize()
+        outs = [torch.empty_like(x) for x in ref]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(outs)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(outs)
+        n_out = 1 if name == "run_own" else 2
+        for i in range(3):
+            for o in outs:
+                o.fill_(0)
+            g.replay()
+            torch.cuda.synchronize()
+            for j in range(n_out):
+                assert torch.equal(outs[j], ref[j]), (name, i, j)
+            junk = torch.randn(1 << 20, device=DEV)
+            assert torch.isfinite(junk.sum())
+            torch.cuda.synchronize()
+        del g
+    for c in caches:
+        c.close()
