@@ -7,10 +7,12 @@ on each of the 24 blocks, append the frame's K/V to the block's pages, evict,
 plan (block 0) and run the paged attention; a non-keyframe attends to the
 cache plus its own K/V on each block without appending them (run_own).  The
 dynamic workload appends every frame under deferred eviction and then
-accepts or rolls it back.  The first
-W frames are untimed and fill the scale pages and the live window, so the K
-timed frames run at steady state.  Inputs (Q, K, V of every block for a bank
-of frames, synthetic N(0,1) bf16) are resident in HBM before the timed region.
+accepts or rolls it back.  Before anything is timed, the stream runs untimed
+until its scale pages and its live window are full (143 frames for the
+518x378 stream: 8 + 64 keyframes at interval 2), whatever W is, and then W
+more untimed frames; the K timed frames therefore run at steady state.
+Inputs (Q, K, V of every block for a bank of frames, synthetic N(0,1) bf16)
+are resident in HBM before the timed region.
 
 Alongside the throughput it reports the roofline of the attention kernel (its
 algorithmic bf16 flops over its duration measured with HIP events on the
@@ -39,7 +41,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=160)
+    ap.add_argument("--warmup", type=int, default=16,
+                    help="untimed frames after the ones that fill the scale pages "
+                         "and the live window")
     ap.add_argument("--workload", default="518x378")
     ap.add_argument("--bank", type=int, default=16, help="distinct input frames")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -68,6 +72,20 @@ def frame_schedule(wl, n):
         else:
             out.append("key" if synth.is_keyframe(wl, f) else "transient")
     return out
+
+
+def fill_frames(wl):
+    """Frames after which the stream's scale pages and live window are full:
+    the frame count at which S + W frames have been committed (keyframes;
+    accepted frames of the dynamic stream)."""
+    need = wl.scale_frames + wl.sliding_window
+    sched = frame_schedule(wl, wl.frames)
+    done = 0
+    for f, kind in enumerate(sched):
+        done += kind in ("key", "accept")
+        if done >= need:
+            return f + 1
+    raise SystemExit(f"{wl.name}: the stream never fills its window")
 
 
 def cpu_baseline(wl, warm_frames, n_blocks_timed):
@@ -230,7 +248,8 @@ def multi_stream(args, wl, R):
         caches = [spkv.PagedKVCache(**wl.cfg_kwargs(), device=dev) for _ in range(R)]
         outs = [[torch.empty((nq, wl.num_heads, wl.head_dim), dtype=torch.bfloat16,
                              device=dev) for _ in range(nb)] for _ in range(R)]
-        total = args.warmup + 2 * args.steps
+        warm = fill_frames(wl) + max(0, args.warmup)
+        total = warm + 2 * args.steps
         sched = frame_schedule(wl, total)
         ev, flops = [], []
 
@@ -275,15 +294,15 @@ def multi_stream(args, wl, R):
                     flops.append(sum(4.0 * nq * (visible(c) + (0 if key else nq)) * hd
                                      for c in caches))
 
-        for f in range(args.warmup):
+        for f in range(warm):
             step(f, False)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for f in range(args.warmup, args.warmup + args.steps):
+        for f in range(warm, warm + args.steps):
             step(f, False)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
-        for f in range(args.warmup + args.steps, total):
+        for f in range(warm + args.steps, total):
             step(f, True)
         torch.cuda.synchronize()
         t_attn = [a.elapsed_time(b) * 1e-3 for a, b in ev]
@@ -311,6 +330,7 @@ def multi_stream(args, wl, R):
                                f"page_size={wl.page_size}, {nq} tokens/frame, "
                                f"keyframe_interval={wl.keyframe_interval}; per block one "
                                f"run_batch over the {R} streams",
+                   "frames_timed": f"{warm}..{warm + args.steps - 1}",
                    "input_bank_frames": nbank},
         "batched": res["batched"],
         "separate": res["separate"],
@@ -323,9 +343,11 @@ def kernel_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic(workload):
+def recorded_traffic(workload, visible_tokens):
     """HBM bytes per attention launch from the committed counter summary, if
-    it was taken on the current kernel source and this workload."""
+    it was taken on the current kernel source and this workload, at a number
+    of visible tokens within 5% of this window's (the launch's bytes grow
+    with them)."""
     try:
         kv = {}
         for line in open(TRAFFIC_FILE):
@@ -335,6 +357,9 @@ def recorded_traffic(workload):
         if kv.get("kernel_source_sha256_16") != kernel_hash():
             return None
         if kv.get("workload") != workload:
+            return None
+        nk = float(kv["visible_tokens"])
+        if abs(nk - visible_tokens) > 0.05 * nk:
             return None
         return float(kv["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -368,7 +393,11 @@ def main():
     S, W = wl.scale_frames, wl.sliding_window
     n_attn = 0 if args.no_events else args.steps     # window B frames
     n_app = 0 if args.no_events else min(args.steps, 20)  # window C frames
-    total = args.warmup + args.steps + n_attn
+    # Untimed frames: those that fill the scale pages and the live window,
+    # then --warmup more, so that every window below is at steady state.
+    n_fill = fill_frames(wl)
+    warm = n_fill + max(0, args.warmup)
+    total = warm + args.steps + n_attn
     sched = frame_schedule(wl, max(total + n_app, wl.frames))
 
     # input bank, resident in HBM before timing
@@ -464,17 +493,24 @@ def main():
             elif kind == "accept":
                 cache.execute_deferred_eviction(b, S, W)
 
-    for f in range(args.warmup):
+    def visible_now(f):
+        # tokens a frame attends to: the plan's, plus its own for a non-keyframe
+        return planned_tokens() + (nq if sched[f] == "transient" else 0)
+
+    for f in range(warm):
         step(f, None)
     torch.cuda.synchronize()
+    assert cache.get_cache_stats(0)[2] == W, "the live window is not full"
+    nk_lo = visible_now(warm - 1)
     t0 = time.perf_counter()
-    for f in range(args.warmup, args.warmup + args.steps):
+    for f in range(warm, warm + args.steps):
         step(f, None)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    nk_hi = visible_now(warm + args.steps - 1)
     use_ev = not args.no_events
     if use_ev:
-        for f in range(args.warmup + args.steps, total):
+        for f in range(warm + args.steps, total):
             step(f, "B")
         for f in range(total, total + n_app):
             step(f, "C")
@@ -517,7 +553,10 @@ def main():
                          + (", dynamic accept/rollback" if wl.dynamic else
                             (", non-keyframes attend to cache + own K/V and skip the append"
                              if wl.keyframe_interval > 1 else ""))),
-            "frames_timed": f"{args.warmup}..{args.warmup + args.steps - 1}",
+            "frames_timed": f"{warm}..{warm + args.steps - 1}",
+            "untimed_frames": (f"{warm}: {n_fill} fill the scale pages and the "
+                               f"{W}-page live window, then --warmup {args.warmup}"),
+            "visible_tokens_timed": [nk_lo, nk_hi],
             "input_bank_frames": nbank,
         },
     }
@@ -529,16 +568,18 @@ def main():
         avg_attn = sum(t_attn) / len(t_attn)
         achieved = sum(flops) / sum(t_attn) / 1e12
         avg_flops = sum(flops) / len(flops)
+        nk_b = [f / (4.0 * nq * hd) for f in flops]
         result["roofline"] = {
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": recorded_traffic(wl.name),
+            "traffic": recorded_traffic(wl.name, sum(nk_b) / len(nk_b)),
             "kernel": "attn_kernel (+ split merge) per run()",
-            "window": (f"frames {args.warmup + args.steps}..{total - 1}, HIP events "
+            "window": (f"frames {warm + args.steps}..{total - 1}, HIP events "
                        f"around each run() on its stream"),
+            "visible_tokens": [int(min(nk_b)), int(max(nk_b))],
             "avg_launch_us": avg_attn * 1e6,
             "algorithmic_flops_per_launch": avg_flops,
         }
@@ -564,7 +605,7 @@ def main():
     del src, dst
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.warmup, args.cpu_blocks)
+        result["cpu_baseline"] = cpu_baseline(wl, warm, args.cpu_blocks)
     print(json.dumps(result), flush=True)
 
 

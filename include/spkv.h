@@ -107,18 +107,22 @@ typedef struct spkv_stats {
  *                          second one frame longer, for run_own).
  *                          run() then processes each (query tile, head) in
  *                          one pass.
- *   full_workspace_bytes = workspace that lets run() split the key range
- *                          across as many workgroups as it wants (up to 32
- *                          splits, each needing (ns+P)*H*(D+2)*4 bytes of
- *                          partial results).  [LB-PERF] "Persistent Workspace
- *                          Pre-allocation" uses 128 MiB; at 1005 query rows
- *                          x 16 heads that holds 31 splits.
  * Any output pointer may be NULL.  INVALID_ARG for an invalid config,
  * UNSUPPORTED for head_dim != 64. */
 SPKV_API int spkv_query_sizes(const spkv_config* cfg, int64_t* max_num_pages,
                               int64_t* pool_bytes_per_block,
-                              int64_t* min_workspace_bytes,
-                              int64_t* full_workspace_bytes);
+                              int64_t* min_workspace_bytes);
+
+/* Workspace that lets run() split the key range of nq query rows across
+ * num_splits workgroups: min_workspace_bytes plus num_splits partial
+ * results of nq * H * (D + 2) * 4 bytes (fp32 O, running maximum and sum).
+ * run() uses up to 32 splits, and fewer when the workspace holds fewer.
+ * [LB-PERF] "Persistent Workspace Pre-allocation" pre-allocates 128 MiB; at
+ * 1005 query rows x 16 heads that holds 31 splits.  This call is an addition
+ * of this library (the pages size no workspace by formula).  1 <= nq <=
+ * 2^20, 1 <= num_splits <= 32, else INVALID_ARG. */
+SPKV_API int spkv_query_workspace(const spkv_config* cfg, int32_t nq, int32_t num_splits,
+                                  int64_t* workspace_bytes);
 
 /* Create a manager.  pool_ptrs: num_blocks device pointers, each to
  * pool_bytes_per_block bytes laid out as above; the library only writes the
@@ -204,8 +208,13 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream);
  * when a block's pool exceeds 4 GiB (pool rows are addressed by 32-bit byte
  * offsets).  Enqueues the attention kernel (and, when the key range is split,
  * a merge kernel) and nothing else, so a run of a planned frame may be
- * captured into a HIP graph and replayed; plan() may not, since it copies
- * the host allocator's state of the moment. */
+ * captured into a HIP graph; plan() may not, since it copies the host
+ * allocator's state of the moment.  A captured run binds the device row map
+ * of the plan that was current at capture (plans alternate between two
+ * slots), its visible-token count and its split: a replay is valid only
+ * while that plan is still the current one, i.e. until the next plan() or
+ * reset().  Replayed after that, it attends over whatever the slot then
+ * holds. */
 SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
                       int32_t nq, float sm_scale, void* hip_stream);
 
@@ -218,8 +227,10 @@ SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
  * append_frame takes).  Neither the pool nor any state changes, so there is
  * nothing to roll back.  Arguments and errors as for run(); own_k and own_v
  * must not overlap out.  UNSUPPORTED when a block's pool exceeds 2 GiB (run()
- * itself takes pools up to 4 GiB).  Enqueues kernels only, as run() does.  Host-only handles pass NULL own_k and
- * own_v and get run()'s checks and result. */
+ * itself takes pools up to 4 GiB).  Enqueues kernels only, as run() does, and
+ * a captured run_own is valid only while its plan is current, as for run().
+ * Host-only handles pass NULL own_k and own_v and get run()'s checks and
+ * result. */
 SPKV_API int spkv_run_own(spkv_handle* h, int32_t block, const void* q, void* out,
                           int32_t nq, float sm_scale, const void* own_k,
                           const void* own_v, void* hip_stream);
@@ -259,7 +270,8 @@ typedef struct {
  * run()'s checks request by request, the first failure's code being
  * returned (host-only handles: UNSUPPORTED once all pass).  Enqueues one
  * attention kernel and, if any range is split, one merge kernel, and nothing
- * else: like run() and run_own(), it may be captured into a HIP graph. */
+ * else: like run() and run_own(), it may be captured into a HIP graph, whose
+ * replays are valid only while every request's plan is still current. */
 SPKV_API int spkv_run_batch(const spkv_request* reqs, int32_t n, void* hip_stream);
 
 /* Split of the key range across workgroups used by run(): 0 = automatic

@@ -49,7 +49,7 @@ ERROR_NAMES = {
 
 # Symbols the header declares (checked by the CPU tests).
 EXPORTED = (
-    "spkv_query_sizes", "spkv_create", "spkv_destroy", "spkv_append_frame",
+    "spkv_query_sizes", "spkv_query_workspace", "spkv_create", "spkv_destroy", "spkv_append_frame",
     "spkv_evict_frames", "spkv_set_defer_eviction",
     "spkv_execute_deferred_eviction", "spkv_rollback_last_frame", "spkv_reset",
     "spkv_plan", "spkv_run", "spkv_run_own", "spkv_run_batch", "spkv_set_num_splits",
@@ -105,7 +105,8 @@ def load_library(path=None):
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     pi32, pi64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
     sig = {
-        "spkv_query_sizes": [ctypes.POINTER(Config), pi64, pi64, pi64, pi64],
+        "spkv_query_sizes": [ctypes.POINTER(Config), pi64, pi64, pi64],
+        "spkv_query_workspace": [ctypes.POINTER(Config), i32, i32, pi64],
         "spkv_create": [ctypes.POINTER(Config), ctypes.POINTER(vp), vp, i64,
                         ctypes.POINTER(vp)],
         "spkv_destroy": [vp],
@@ -156,15 +157,30 @@ def make_config(**kw):
     return c
 
 
-def query_sizes(**cfg):
-    """(max_num_pages, pool_bytes_per_block, min_workspace_bytes,
-    full_workspace_bytes) of a configuration."""
+MAX_SPLITS = 32
+
+
+def query_workspace(nq, num_splits, **cfg):
+    """Workspace bytes that let run() split nq query rows num_splits ways."""
     lib = load_library()
     c = make_config(**cfg)
-    out = [ctypes.c_int64() for _ in range(4)]
+    out = ctypes.c_int64()
+    _check(lib.spkv_query_workspace(ctypes.byref(c), int(nq), int(num_splits),
+                                    ctypes.byref(out)), "spkv_query_workspace")
+    return out.value
+
+
+def query_sizes(**cfg):
+    """(max_num_pages, pool_bytes_per_block, min_workspace_bytes,
+    full_workspace_bytes) of a configuration; the last is the workspace that
+    lets run() split one frame's queries the most ways it does (32)."""
+    lib = load_library()
+    c = make_config(**cfg)
+    out = [ctypes.c_int64() for _ in range(3)]
     _check(lib.spkv_query_sizes(ctypes.byref(c), *[ctypes.byref(x) for x in out]),
            "spkv_query_sizes")
-    return tuple(x.value for x in out)
+    tpf = int(cfg["num_special_tokens"]) + int(cfg["patch_tokens"])
+    return tuple(x.value for x in out) + (query_workspace(tpf, MAX_SPLITS, **cfg),)
 
 
 class PagedKVCache:

@@ -53,8 +53,15 @@ bool to_geometry(const spkv_config* c, spkv::Geometry* g) {
 
 struct Sizes {
   int64_t max_num_pages, pool_bytes, table_bytes, rowmap_entries,
-      rowmap_bytes, rowmap_own_bytes, min_ws, per_split, full_ws;
+      rowmap_bytes, rowmap_own_bytes, min_ws;
 };
+
+// Split partials of nq query rows: fp32 O and (m, l) per (query, head) row
+// and split.
+int64_t partial_bytes(const spkv::Geometry& g, int64_t nq, int64_t splits) {
+  const int64_t rows = nq * g.num_heads;
+  return round_up(rows * g.head_dim * 4 * splits, kAlign) + round_up(rows * 8 * splits, kAlign);
+}
 
 Sizes sizes_of(const spkv::Geometry& g) {
   Sizes s;
@@ -72,10 +79,6 @@ Sizes sizes_of(const spkv::Geometry& g) {
       round_up((round_up(int64_t(g.max_num_pages) * g.page_size + g.tokens_per_frame,
                          spkv::kAttnKeyTile) + spkv::kRowmapPad) * 4, kAlign);
   s.min_ws = 2 * s.table_bytes + 2 * s.rowmap_bytes + 2 * s.rowmap_own_bytes;
-  // Partial O (fp32, D per row) and (m, l) for every (query, head) row.
-  const int64_t rows = int64_t(g.tokens_per_frame) * g.num_heads;
-  s.per_split = round_up(rows * g.head_dim * 4, kAlign) + round_up(rows * 8, kAlign);
-  s.full_ws = s.min_ws + kMaxSplits * s.per_split;
   return s;
 }
 
@@ -147,8 +150,7 @@ SPKV_API const char* spkv_error_string(int code) {
 
 SPKV_API int spkv_query_sizes(const spkv_config* cfg, int64_t* max_num_pages,
                               int64_t* pool_bytes_per_block,
-                              int64_t* min_workspace_bytes,
-                              int64_t* full_workspace_bytes) {
+                              int64_t* min_workspace_bytes) {
   spkv::Geometry g;
   if (!to_geometry(cfg, &g)) return SPKV_ERR_INVALID_ARG;
   if (g.head_dim != 64) return SPKV_ERR_UNSUPPORTED;
@@ -156,7 +158,18 @@ SPKV_API int spkv_query_sizes(const spkv_config* cfg, int64_t* max_num_pages,
   if (max_num_pages) *max_num_pages = s.max_num_pages;
   if (pool_bytes_per_block) *pool_bytes_per_block = s.pool_bytes;
   if (min_workspace_bytes) *min_workspace_bytes = s.min_ws;
-  if (full_workspace_bytes) *full_workspace_bytes = s.full_ws;
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_query_workspace(const spkv_config* cfg, int32_t nq, int32_t num_splits,
+                                  int64_t* workspace_bytes) {
+  spkv::Geometry g;
+  if (!to_geometry(cfg, &g)) return SPKV_ERR_INVALID_ARG;
+  if (g.head_dim != 64) return SPKV_ERR_UNSUPPORTED;
+  if (nq < 1 || nq > kMaxQueryRows || num_splits < 1 || num_splits > kMaxSplits)
+    return SPKV_ERR_INVALID_ARG;
+  if (workspace_bytes)
+    *workspace_bytes = sizes_of(g).min_ws + partial_bytes(g, nq, num_splits);
   return SPKV_OK;
 }
 
@@ -433,11 +446,8 @@ spkv::AttnArgs make_run(spkv_handle* h, int32_t block, const void* q, void* out,
   // Split partials: fp32 O and (m, l) per (query, head) row and split, in
   // the workspace after the plan's buffers.
   const int64_t rows = int64_t(nq) * g.num_heads;
-  auto partial_bytes = [&](int64_t sp) {
-    return round_up(rows * g.head_dim * 4 * sp, kAlign) + round_up(rows * 8 * sp, kAlign);
-  };
   int64_t cap = kMaxSplits;
-  while (cap > 1 && partial_bytes(cap) > h->ws_bytes - h->sz.min_ws) --cap;
+  while (cap > 1 && partial_bytes(g, nq, cap) > h->ws_bytes - h->sz.min_ws) --cap;
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, cap));
   splits = std::min<int64_t>(splits, shape.n_ktiles);
   const int64_t tiles_per_split = (shape.n_ktiles + splits - 1) / splits;

@@ -536,9 +536,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const Runs<NB> runs) 
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
 
+  // A run without own rows (a plain run() batched beside a run_own()) never
+  // takes the own-row branch: its byte offsets may use the top bit.
+  const int n_cached = OWN && a.own_k ? a.n_cached : INT_MAX;
 #define SPKV_RUN(NT, G)                                                                \
   run_phases<NT, G, OWN>(d, a.rowmap, rm_lds, lds, lds_addr, t_begin, t_end, row_bytes, f, \
-                         half, c, qf, o_acc, m_run, l_run, a.n_cached)
+                         half, c, qf, o_acc, m_run, l_run, n_cached)
   if (wave < 4) {
     if (n_active == 2) SPKV_RUN(2, 0);
     else if (n_active == 1) SPKV_RUN(1, 0);

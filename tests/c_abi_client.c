@@ -44,6 +44,15 @@ int main(int argc, char** argv) {
   c.max_total_frames = atoi(argv[10]);
   frames = atoi(argv[11]);
 
+  {
+    int64_t mnp = 0, pool = 0, wmin = 0, w1 = 0, w8 = 0;
+    rc = spkv_query_sizes(&c, &mnp, &pool, &wmin);
+    printf("query_sizes %d %lld %lld\n", rc, (long long)mnp, (long long)pool);
+    rc = spkv_query_workspace(&c, c.num_special_tokens + c.patch_tokens, 1, &w1) ||
+         spkv_query_workspace(&c, c.num_special_tokens + c.patch_tokens, 8, &w8);
+    printf("query_workspace %d %d %d\n", rc, (int)(w1 > wmin), (int)(w8 - wmin > 7 * (w1 - wmin)));
+    printf("query_workspace_bad %d\n", spkv_query_workspace(&c, 1, 33, &w1));
+  }
   rc = spkv_create(&c, NULL, NULL, 0, &h);
   printf("create %d\n", rc);
   if (rc != SPKV_OK) return 1;

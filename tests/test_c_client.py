@@ -57,6 +57,10 @@ def test_c_client_runs_the_worked_example(client, golden_dir):
         assert free == row["free"], line
         assert stats == row["stats"], line
     codes = {v: k for k, v in spkv.ERROR_NAMES.items()}
+    mnp, pool, _, _ = spkv.query_sizes(**cfg)
+    assert kv["query_sizes"] == f"0 {mnp} {pool}"
+    assert kv["query_workspace"] == "0 1 1"
+    assert int(kv["query_workspace_bad"]) == codes["INVALID_ARG"]
     assert int(kv["create"]) == 0
     assert int(kv["run_before_plan"]) == codes["NOT_PLANNED"]
     assert int(kv["plan_empty"]) == codes["EMPTY"]

@@ -311,6 +311,55 @@ def test_pool_offsets_up_to_4gib_and_pool_size_limits():
     cache.close()
 
 
+def test_run_batch_plain_run_on_4gib_pool_beside_run_own():
+    """A batch that holds a run_own() request launches the kernel variant that
+    reads the caller's own rows; a plain run() request in the same launch
+    must still read its row offsets as pool rows, also those with the top bit
+    set.  The plain request runs on the 4 GiB pool, whose special pages lie
+    at byte offsets 4094 MiB and up; the run_own request on a small stream.
+    Both against the oracle, with forced 1 and 3 splits."""
+    need_gpu()
+    import streaming_paged_kv_amd as spkv
+    big = POOL_4GIB
+    small = synth.WORKLOADS["tiny"].with_(name="tiny-own", seed=33)
+    cfg_b = OracleConfig(**big.cfg_kwargs())
+    cfg_s = OracleConfig(**small.cfg_kwargs())
+    ob = PagePoolOracle(cfg_b, track_pool=[0])
+    osm = PagePoolOracle(cfg_s, track_pool=[0])
+    cb, cs = new_cache(big), new_cache(small)
+    sm = 0.125
+    for f in range(3):
+        for wl, c, o in ((big, cb, ob), (small, cs, osm)):
+            q, k, v = synth.frame_qkv(wl, f, 0, device=DEV)
+            c.append_frame(0, k, v)
+            c.evict_frames(0, wl.scale_frames, wl.sliding_window)
+            o.append_frame(0, synth.bf16_bits(k), synth.bf16_bits(v))
+            o.evict_frames(0, wl.scale_frames, wl.sliding_window)
+    cb.plan()
+    cs.plan()
+    pb, ps = ob.plan(), osm.plan()
+    qb = synth.frame_qkv(big, 10, 0, device=DEV)[0]
+    qs, ks, vs = synth.frame_qkv(small, 10, 0, device=DEV)
+    ref_b = paged_attention(ob.pools[0], pb, cfg_b, synth.bf16_bits(qb), sm)
+    from oracle.attention import paged_attention_with_own
+    ref_s = paged_attention_with_own(osm.pools[0], ps, cfg_s, synth.bf16_bits(qs),
+                                     synth.bf16_bits(ks), synth.bf16_bits(vs), sm)
+    assert cb.get_plan()[0][-1] == 4094
+    for splits in (1, 3):
+        cb.set_num_splits(splits)
+        cs.set_num_splits(splits)
+        log(f"  4 GiB run() beside a run_own(), splits {splits}")
+        outs = spkv.run_batch([dict(cache=cb, block=0, q=qb, sm_scale=sm),
+                               dict(cache=cs, block=0, q=qs, k=ks, v=vs, sm_scale=sm)])
+        torch.cuda.synchronize()
+        H.compare(outs[0], ref_b, ("4 GiB run in an own batch", splits))
+        H.compare(outs[1], ref_s, ("run_own beside a 4 GiB run", splits))
+    cb.close()
+    cs.close()
+    del cb
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("mode", ["all_far_below", "all_far_above", "mixed"])
 def test_extreme_logits(mode):
     """Scores far from 0: every score of a frame about -50 (every p would
@@ -350,6 +399,57 @@ def test_extreme_logits(mode):
         torch.cuda.synchronize()
         ref = paged_attention(o.pools[0], pl, cfg, synth.bf16_bits(q), 0.125)
         H.compare(out, ref, ("extreme", mode, f))
+    cache.close()
+
+
+@pytest.mark.parametrize("name", ["224x224", "518x378"])
+def test_planted_sharp_keys_at_full_geometry(name):
+    """Sharp softmax at the full-size geometries (one block, the window full
+    and evicting): keys planted along chosen query rows of the last frame, in
+    a scale frame's page, a live page and a special slot, plus one row with
+    two nearly equal planted keys, so that a few keys carry almost all of the
+    weight and the output is a visible value vector rather than an average of
+    ~1e-3.  Sampled rows (the planted ones among them) of all heads against
+    the oracle, at the automatic split and at a forced 5-way split."""
+    need_gpu()
+    base = synth.WORKLOADS[name]
+    wl = base.with_(name=f"{name}-sharp", num_blocks=1, keyframe_interval=1,
+                    frames=base.scale_frames + base.sliding_window + 8)
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    o = PagePoolOracle(cfg, track_pool=[0])
+    cache = new_cache(wl)
+    last = wl.frames - 1
+    q_fin = synth.frame_qkv(wl, last, 0, device=DEV)[0]
+    # (frame, token of the frame, query row of the last frame, gain)
+    nq = wl.tokens_per_frame
+    plants = [(3, 6 + 100, 11, 4.0),            # scale page
+              (last - 5, 6 + 200, 300 % nq, 4.0),   # live page
+              (40, 2, 600 % nq, 4.0),           # special slot (register 2)
+              (50, 6 + 17, 7, 3.0), (60, 6 + 18, 7, 2.95)]   # two close keys
+    for f in range(wl.frames):
+        q, k, v = synth.frame_qkv(wl, f, 0, device=DEV)
+        for pf, tok, row, gain in plants:
+            if pf == f:
+                k = k.clone()
+                k[tok] = (q_fin[row].float() * gain).to(torch.bfloat16)
+        cache.append_frame(0, k, v)
+        cache.evict_frames(0, wl.scale_frames, wl.sliding_window)
+        o.append_frame(0, synth.bf16_bits(k), synth.bf16_bits(v))
+        o.evict_frames(0, wl.scale_frames, wl.sliding_window)
+    assert cache.get_cache_stats(0)[2] == wl.sliding_window
+    cache.plan()
+    pl = o.plan()
+    rows = sorted(set(H.sample_rows(wl.tokens_per_frame, extra=16, seed=9)) |
+                  {p[2] for p in plants})
+    ref = paged_attention(o.pools[0], pl, cfg, synth.bf16_bits(q_fin[rows]), 0.125)
+    sharp = np.abs(ref).max(axis=(1, 2))
+    assert (sharp[[rows.index(p[2]) for p in plants]] > 0.5).all()   # planted rows are sharp
+    for splits in (0, 5):
+        cache.set_num_splits(splits)
+        out = cache.run(0, q_fin, sm_scale=0.125)
+        torch.cuda.synchronize()
+        log(f"  {name} sharp keys, splits {splits}")
+        H.compare(out[rows], ref, ("sharp", name, splits))
     cache.close()
 
 

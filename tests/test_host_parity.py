@@ -133,7 +133,7 @@ def test_full_stream_schedules_match_oracle(name):
     S, W = wl.scale_frames, wl.sliding_window
     decisions = synth.accept_decisions(wl) if wl.dynamic else None
     nb = wl.num_blocks
-    frames = min(wl.frames, 1200)
+    frames = wl.frames
     if wl.dynamic:
         o.set_defer_eviction(True)
         c.set_defer_eviction(True)

@@ -18,7 +18,9 @@ import oracle.attention as att
 import oracle.pagepool as pp
 from oracle import OracleConfig, PagePoolOracle
 
+import oracle.bf16 as bf
 import test_oracle_attention as ta
+import test_oracle_bf16 as tb
 import test_oracle_pins as tp
 
 
@@ -43,6 +45,10 @@ def _pin_suite(golden_dir):
         ta.test_matches_torch_sdpa_float64,
         ta.test_two_tokens_closed_form,
         ta.test_gather_reads_only_valid_slots,
+        lambda: [tb.test_widening_hand_values(b, x) for b, x in tb.HAND],
+        tb.test_widening_signed_zero_and_infinities,
+        tb.test_widening_every_pattern_matches_torch,
+        lambda: [tb.test_narrowing_rounds_to_nearest_even(x, b) for x, b in tb.NARROW],
     ]
 
 
@@ -218,6 +224,51 @@ def _m12(mp):
             blk.last = (p, "scale")
         return r
     mp.setattr(pp.PagePoolOracle, "append_frame", append)
+
+
+def _patch_widening(mp, fn):
+    mp.setattr(bf, "bf16_bits_to_f64", fn)
+    mp.setattr(att, "bf16_bits_to_f64", fn)
+
+
+@mutant("bf16 widening shifts the uint16 without widening it first")
+def _m13(mp):
+    def widen(bits):
+        b = np.asarray(bits, dtype=np.uint16)
+        return (b << np.uint16(16)).astype(np.uint32).view(np.float32).astype(np.float64)
+    _patch_widening(mp, widen)
+
+
+@mutant("bf16 widening shifts by 15")
+def _m14(mp):
+    def widen(bits):
+        b = np.asarray(bits, dtype=np.uint16)
+        return (b.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+    _patch_widening(mp, widen)
+
+
+@mutant("bf16 pattern read as float16")
+def _m15(mp):
+    def widen(bits):
+        return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    _patch_widening(mp, widen)
+
+
+@mutant("bf16 narrowing truncates instead of rounding")
+def _m16(mp):
+    def narrow(x):
+        f = np.asarray(x, dtype=np.float64).astype(np.float32)
+        return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    mp.setattr(bf, "f64_to_bf16_bits", narrow)
+
+
+@mutant("bf16 narrowing rounds ties away from zero")
+def _m17(mp):
+    def narrow(x):
+        f = np.asarray(x, dtype=np.float64).astype(np.float32)
+        u = f.view(np.uint32).astype(np.uint64)
+        return ((u + np.uint64(0x8000)) >> np.uint64(16)).astype(np.uint16)
+    mp.setattr(bf, "f64_to_bf16_bits", narrow)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
