@@ -218,6 +218,23 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream);
 SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
                       int32_t nq, float sm_scale, void* hip_stream);
 
+/* run() for callers that cannot allocate device memory or size a workspace
+ * for it (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same attention, with the key-range split's partial
+ * results kept in device memory that the library itself holds, a 48 MiB
+ * array per GPU (allocated when the library's code is loaded on that GPU and
+ * held until the process ends), instead of in the handle's workspace.  So a
+ * handle created with only min_workspace_bytes still gets run()'s split.
+ * The call allocates nothing.  Limit: nq <= 48 MiB / (2 * H * (D + 2) * 4)
+ * rounded down (two splits of partials; 5957 rows at H = 16), else
+ * SPKV_ERR_WORKSPACE and nothing is enqueued.  Every call on one GPU shares
+ * that GPU's array, whatever the handle: two calls whose kernels overlap in
+ * time on one GPU (different streams, no ordering between them) race on it
+ * and give wrong results; calls ordered on one stream are safe.  Arguments,
+ * other errors and the plan contract are run()'s. */
+SPKV_API int spkv_run_noalloc(spkv_handle* h, int32_t block, const void* q, void* out,
+                              int32_t nq, float sm_scale, void* hip_stream);
+
 /* run(block) for a frame that attends to the cache without joining it: the
  * non-keyframe case of [LB-SLOT] "进阶：光流关键帧与回滚机制" (it attends to
  * the cache plus its own K/V, and its K/V are not stored) and the

@@ -52,7 +52,7 @@ EXPORTED = (
     "spkv_query_sizes", "spkv_query_workspace", "spkv_create", "spkv_destroy", "spkv_append_frame",
     "spkv_evict_frames", "spkv_set_defer_eviction",
     "spkv_execute_deferred_eviction", "spkv_rollback_last_frame", "spkv_reset",
-    "spkv_plan", "spkv_run", "spkv_run_own", "spkv_run_batch", "spkv_set_num_splits",
+    "spkv_plan", "spkv_run", "spkv_run_noalloc", "spkv_run_own", "spkv_run_batch", "spkv_set_num_splits",
     "spkv_get_cache_stats",
     "spkv_get_plan", "spkv_get_block_state", "spkv_error_string",
 )
@@ -118,6 +118,7 @@ def load_library(path=None):
         "spkv_reset": [vp],
         "spkv_plan": [vp, vp],
         "spkv_run": [vp, i32, vp, vp, i32, ctypes.c_float, vp],
+        "spkv_run_noalloc": [vp, i32, vp, vp, i32, ctypes.c_float, vp],
         "spkv_run_own": [vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp],
         "spkv_run_batch": [ctypes.POINTER(Request), i32, vp],
         "spkv_set_num_splits": [vp, i32],
@@ -318,6 +319,26 @@ class PagedKVCache:
         op = self._frame_tensor(out, "out", n)
         _check(self.lib.spkv_run(self._h, block, qp, op, n, float(sm_scale),
                                  _stream_ptr(stream)), "spkv_run")
+        return out
+
+    def run_noalloc(self, block, q=None, out=None, sm_scale=None, nq=None, stream=None):
+        """run() with the split partials in the library's own device memory
+        (spkv_run_noalloc): nothing is allocated, and the handle's workspace
+        need only be the minimum.  Calls on one GPU share that memory."""
+        if sm_scale is None:
+            sm_scale = self.cfg["head_dim"] ** -0.5
+        if self.host_only:
+            n = self.tokens_per_frame if nq is None else nq
+            _check(self.lib.spkv_run_noalloc(self._h, block, None, None, n, sm_scale, None),
+                   "spkv_run_noalloc")
+            return None
+        n = q.shape[0] if nq is None else nq
+        qp = self._frame_tensor(q, "q", n)
+        if out is None:
+            out = torch.empty_like(q)
+        op = self._frame_tensor(out, "out", n)
+        _check(self.lib.spkv_run_noalloc(self._h, block, qp, op, n, float(sm_scale),
+                                         _stream_ptr(stream)), "spkv_run_noalloc")
         return out
 
     def run_own(self, block, q=None, k=None, v=None, out=None, sm_scale=None, nq=None,

@@ -124,6 +124,7 @@ struct spkv_handle {
   int plan_slot = 0;                 // slot holding the current plan
   int next_slot = 0;
   char* partials = nullptr;
+  char* scratch = nullptr;           // this device's library-held partials
   int forced_splits = 0;
   int num_cus = 256;
 };
@@ -223,6 +224,11 @@ SPKV_API int spkv_create(const spkv_config* cfg, void* const* pool_ptrs,
   h->dev_rowmap_own[1] = reinterpret_cast<uint32_t*>(
       h->ws + 2 * sz.table_bytes + 2 * sz.rowmap_bytes + sz.rowmap_own_bytes);
   h->partials = h->ws + sz.min_ws;
+  // The device address of run_noalloc()'s scratch, looked up once per device
+  // with that device current.
+  void* scratch = nullptr;
+  if (spkv::scratch_address(&scratch) != hipSuccess) return SPKV_ERR_HIP;
+  h->scratch = static_cast<char*>(scratch);
   if (hipHostMalloc(reinterpret_cast<void**>(&h->stage),
                     size_t(2) * g.max_num_pages * sizeof(int32_t),
                     hipHostMallocDefault) != hipSuccess) {
@@ -436,18 +442,28 @@ int check_run(spkv_handle* h, int32_t block, const void* q, void* out, int32_t n
   return SPKV_OK;
 }
 
+// Where a run's split partials go: the workspace after the plan's buffers,
+// or the library's scratch (run_noalloc).
+struct Partials {
+  char* base;
+  int64_t bytes;
+};
+
+Partials workspace_partials(const spkv_handle* h) {
+  return Partials{h->partials, h->ws_bytes - h->sz.min_ws};
+}
+
 // Kernel arguments of a checked request with `want` splits of its key range
-// (before the limits of the workspace and of the key tiles).
+// (before the limits of the partials' buffer and of the key tiles).
 spkv::AttnArgs make_run(spkv_handle* h, int32_t block, const void* q, void* out,
                         int32_t nq, float sm_scale, const void* own_k, const void* own_v,
-                        const RunShape& shape, int64_t want) {
+                        const RunShape& shape, int64_t want, Partials part) {
   const spkv::Geometry& g = h->g;
   int64_t splits = h->forced_splits > 0 ? h->forced_splits : want;
-  // Split partials: fp32 O and (m, l) per (query, head) row and split, in
-  // the workspace after the plan's buffers.
+  // Split partials: fp32 O and (m, l) per (query, head) row and split.
   const int64_t rows = int64_t(nq) * g.num_heads;
   int64_t cap = kMaxSplits;
-  while (cap > 1 && partial_bytes(g, nq, cap) > h->ws_bytes - h->sz.min_ws) --cap;
+  while (cap > 1 && partial_bytes(g, nq, cap) > part.bytes) --cap;
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, cap));
   splits = std::min<int64_t>(splits, shape.n_ktiles);
   const int64_t tiles_per_split = (shape.n_ktiles + splits - 1) / splits;
@@ -461,9 +477,9 @@ spkv::AttnArgs make_run(spkv_handle* h, int32_t block, const void* q, void* out,
   a.rowmap = own ? h->dev_rowmap_own[h->plan_slot] : h->dev_rowmap[h->plan_slot];
   a.q = static_cast<const uint16_t*>(q);
   a.out = static_cast<uint16_t*>(out);
-  a.part_o = reinterpret_cast<float*>(h->partials);
+  a.part_o = reinterpret_cast<float*>(part.base);
   a.part_ml = reinterpret_cast<float*>(
-      h->partials + round_up(rows * g.head_dim * 4 * splits, kAlign));
+      part.base + round_up(rows * g.head_dim * 4 * splits, kAlign));
   a.nq = nq;
   a.num_heads = g.num_heads;
   a.page_size = g.page_size;
@@ -475,16 +491,28 @@ spkv::AttnArgs make_run(spkv_handle* h, int32_t block, const void* q, void* out,
   return a;
 }
 
+// Query rows run_noalloc() takes: the library's scratch must hold two
+// splits of their partials.
+int64_t noalloc_max_rows(const spkv::Geometry& g) {
+  int64_t n = spkv::kScratchBytes / (2 * int64_t(g.num_heads) * (g.head_dim + 2) * 4);
+  while (n > 0 && partial_bytes(g, n, 2) > spkv::kScratchBytes) --n;
+  return n;
+}
+
 int run_impl(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq,
-             float sm_scale, const void* own_k, const void* own_v, void* hip_stream) {
+             float sm_scale, const void* own_k, const void* own_v, void* hip_stream,
+             bool noalloc = false) {
   RunShape shape;
   const int rc = check_run(h, block, q, out, nq, sm_scale, own_k, own_v, &shape);
   if (rc != SPKV_OK) return rc;
+  if (noalloc && nq > noalloc_max_rows(h->g)) return SPKV_ERR_WORKSPACE;
   // One resident workgroup per CU; each split keeps >= 4 key tiles.
   int64_t want = (int64_t(h->num_cus) + shape.units - 1) / shape.units;
   want = std::min<int64_t>(want, std::max<int64_t>(1, shape.n_ktiles / 4));
+  const Partials part = noalloc ? Partials{h->scratch, spkv::kScratchBytes}
+                                : workspace_partials(h);
   const spkv::AttnArgs a =
-      make_run(h, block, q, out, nq, sm_scale, own_k, own_v, shape, want);
+      make_run(h, block, q, out, nq, sm_scale, own_k, own_v, shape, want, part);
   DeviceGuard guard(h->device);
   if (spkv::launch_attention(a, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
     return SPKV_ERR_HIP;
@@ -504,6 +532,11 @@ extern "C" {
 SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
                       int32_t nq, float sm_scale, void* hip_stream) {
   return run_impl(h, block, q, out, nq, sm_scale, nullptr, nullptr, hip_stream);
+}
+
+SPKV_API int spkv_run_noalloc(spkv_handle* h, int32_t block, const void* q, void* out,
+                              int32_t nq, float sm_scale, void* hip_stream) {
+  return run_impl(h, block, q, out, nq, sm_scale, nullptr, nullptr, hip_stream, true);
 }
 
 SPKV_API int spkv_run_own(spkv_handle* h, int32_t block, const void* q, void* out,
@@ -581,7 +614,7 @@ SPKV_API int spkv_run_batch(const spkv_request* reqs, int32_t n, void* hip_strea
     const spkv_request& r = reqs[i];
     const int64_t want = (shape[i].n_ktiles + per_item - 1) / per_item;
     runs[i] = make_run(r.handle, r.block, r.q, r.out, r.nq, r.sm_scale, r.own_k, r.own_v,
-                       shape[i], want);
+                       shape[i], want, workspace_partials(r.handle));
   }
   DeviceGuard guard(reqs[0].handle->device);
   if (spkv::launch_attention_batch(runs, n, static_cast<hipStream_t>(hip_stream)) !=

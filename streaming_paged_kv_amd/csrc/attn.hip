@@ -52,8 +52,14 @@
 //    dealt to the 8 XCDs round-robin), where they share that XCD's L2.
 #include "kernels.h"
 
+#include <mutex>
+
 namespace spkv {
 namespace {
+
+// run_noalloc()'s split partials.  In host code `scratch` names a host-side
+// stand-in: its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -690,6 +696,25 @@ __global__ __launch_bounds__(256) void merge_batch_kernel(const Merges<NB> m) {
 }
 
 }  // namespace
+
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_expand(const PlanArgs& p, hipStream_t stream) {
   const int n = max(p.n_out, p.n_out_own);

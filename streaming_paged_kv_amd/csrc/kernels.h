@@ -78,6 +78,14 @@ struct AttnArgs {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 
+// Device memory the library itself holds for run_noalloc(): the split
+// partials of one run, in a file-scope array of attn.hip (one copy per GPU,
+// held until the process ends).  scratch_address() returns the calling
+// thread's current device's copy; it looks the address up once per device
+// and caches it.
+constexpr int64_t kScratchBytes = int64_t(48) << 20;
+hipError_t scratch_address(void** out);
+
 // Several runs (independent streams, each with its own pool, row map and
 // partials) in one attention launch and at most one merge launch.  Runs are
 // validated by the caller; n <= kMaxBatchRuns.
