@@ -26,12 +26,14 @@ def gather_visible(pool, plan, cfg):
     ``pool`` is the block's uint16 [max_num_pages, 2, page_size, H, D] array.
     Only the valid slots of each page are read (reading R4/R5): the tail of a
     padded patch page and the unused tail of a special page are never part of
-    the sequence ([LB-KV] "Physical Page Layout and Indexing").
+    the sequence ([LB-KV] "Physical Page Layout and Indexing").  Of a special
+    page's slots, those of special tokens that eviction took out of view
+    (reading R13) are skipped.
     """
     ks, vs = [], []
-    for page, n in zip(plan.table, plan.page_lengths(cfg)):
-        ks.append(pool[page, 0, 0:n])
-        vs.append(pool[page, 1, 0:n])
+    for page, slots in zip(plan.table, plan.visible_slots(cfg)):
+        ks.append(pool[page, 0, slots])
+        vs.append(pool[page, 1, slots])
     k = bf16_bits_to_f64(np.concatenate(ks, axis=0))
     v = bf16_bits_to_f64(np.concatenate(vs, axis=0))
     return k, v

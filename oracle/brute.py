@@ -12,7 +12,9 @@ plan) and Part 2 (the gather) together:
   ([LB-SLOT] "keyframes：滑动窗口 slot 的进出规则");
 * every committed frame keeps its special tokens, and they come after all
   patch tokens ([LB-SLOT] "特殊 token 流"; [LB-KV] "Patch Pages vs. Special
-  Pages");
+  Pages") -- except that a frame whose patch tokens have left keeps only the
+  first ``kept`` of them when the stream's eviction flags say so ([LB-KV]
+  "Append and Evict API", specials optionally preserved; reading R13);
 * a frame that is not (yet) committed -- a non-keyframe, or a frame whose
   keyframe decision is pending under deferred eviction -- attends to the cache
   plus its own K/V ([LB-SLOT] "keyframes" table, non-keyframe row; reading R6):
@@ -29,10 +31,11 @@ from .attention import dense_attention
 
 
 class BruteForceStream:
-    def __init__(self, scale_frames, sliding_window, num_special_tokens):
+    def __init__(self, scale_frames, sliding_window, num_special_tokens, kept=None):
         self.s = scale_frames
         self.w = sliding_window
         self.ns = num_special_tokens
+        self.kept = num_special_tokens if kept is None else kept
         self.committed_k = []
         self.committed_v = []
 
@@ -62,8 +65,11 @@ class BruteForceStream:
         if own_k is not None:
             ks.append(np.asarray(own_k, dtype=np.float64)[ns:])
             vs.append(np.asarray(own_v, dtype=np.float64)[ns:])
-        ks += [f[:ns] for f in self.committed_k]
-        vs += [f[:ns] for f in self.committed_v]
+        held = set(patch_frames)
+        for i in range(len(self.committed_k)):
+            n = ns if i in held else self.kept
+            ks.append(self.committed_k[i][:n])
+            vs.append(self.committed_v[i][:n])
         if own_k is not None:
             ks.append(np.asarray(own_k, dtype=np.float64)[:ns])
             vs.append(np.asarray(own_v, dtype=np.float64)[:ns])

@@ -15,6 +15,9 @@ Per block the state is
   live   deque of patch page ids of the sliding window, oldest first
   nsf    number of frames whose special tokens are in the special stream
   last   (page, 'scale'|'live') of the most recent append, or None
+  frame_of  page id -> index (in the special stream) of the frame it holds
+  spec_vis  per committed frame, how many of its special tokens are visible
+  flags  (cross_frame_special, camera_only) of the block's last evict_frames
 plus one manager-wide ``defer`` flag, and optionally the pool bytes
   pool   uint16 [max_num_pages, 2, page_size, H, D]  (bf16 patterns, 0=K 1=V)
 """
@@ -137,6 +140,9 @@ class Plan:
     scale: tuple = field(default=())
     live: tuple = field(default=())
     nsf: int = 0
+    # Per committed frame, how many of its special tokens are visible
+    # (reading R13); all of them unless an eviction flag removed some.
+    spec_vis: tuple = field(default=())
 
     def page_lengths(self, cfg):
         """Valid tokens of each table entry, derived from its position.
@@ -157,8 +163,31 @@ class Plan:
                 out.append(self.last_page_len)
         return out
 
+    def visible_slots(self, cfg):
+        """For each table entry, the list of its valid slots that are visible.
+
+        Patch pages: all of their valid slots.  Special pages: slot o of
+        special page p holds token o % num_special of frame
+        (p - M) * frames_per_special_page + o // num_special ([LB-SLOT]
+        "特殊 token 流"), and it is visible when that token's index is below the
+        frame's count in spec_vis (reading R13: the camera token is the first).
+        """
+        ns, fpp, m = cfg.num_special_tokens, cfg.frames_per_special_page, cfg.num_patch_pages
+        out = []
+        for i, (page, n) in enumerate(zip(self.table, self.page_lengths(cfg))):
+            if i < self.n_patch:
+                out.append(list(range(n)))
+                continue
+            keep = []
+            for o in range(n):
+                frame = (page - m) * fpp + o // ns
+                if o % ns < self.spec_vis[frame]:
+                    keep.append(o)
+            out.append(keep)
+        return out
+
     def num_visible_tokens(self, cfg):
-        return int(sum(self.page_lengths(cfg)))
+        return int(sum(len(x) for x in self.visible_slots(cfg)))
 
 
 class _Block:
@@ -168,6 +197,22 @@ class _Block:
         self.live = deque()
         self.nsf = 0
         self.last = None
+        self.frame_of = {}
+        self.spec_vis = []
+        self.flags = (1, 0)             # reading R13: the pages' defaults
+
+
+def special_tokens_kept(cfg, cross_frame_special, camera_only):
+    """How many of an evicted frame's special tokens stay visible (reading
+    R13).  [LB-KV] "Append and Evict API": eviction recycles the oldest patch
+    pages "while optionally preserving special tokens"; [LB-SLOT] "特殊 token
+    流": kept specials are where cross-frame context comes from, the camera
+    tokens of any earlier frame in particular.  cross_frame_special=1 keeps
+    them (all of them, or with camera_only=1 the camera token, the first of
+    the frame's specials); cross_frame_special=0 keeps none."""
+    if not cross_frame_special:
+        return 0
+    return 1 if camera_only else cfg.num_special_tokens
 
 
 class PagePoolOracle:
@@ -261,6 +306,8 @@ class PagePoolOracle:
             pool[s_page, 0, s_slot:s_slot + ns] = k[0:ns]
             pool[s_page, 1, s_slot:s_slot + ns] = v[0:ns]
 
+        blk.frame_of[p] = blk.nsf
+        blk.spec_vis.append(c.num_special_tokens)   # a resident frame: all visible
         blk.nsf += 1
         blk.last = (p, where)
         return p, s_page, s_slot
@@ -268,10 +315,15 @@ class PagePoolOracle:
     def _evict_to(self, blk, sliding_window):
         """Pop the oldest live pages to the tail of the free list while the
         window is over its limit ([LB-SLOT] "keyframes：滑动窗口 slot 的进出规则";
-        [LB-KV] "How is memory bounded in streaming mode?")."""
+        [LB-KV] "How is memory bounded in streaming mode?").  The frame a page
+        held keeps as many visible special tokens as the block's eviction
+        flags say (reading R13); its bytes stay in the special stream."""
         moved = 0
+        kept = special_tokens_kept(self.cfg, *blk.flags)
         while len(blk.live) > sliding_window:
-            blk.free.append(blk.live.popleft())   # reading R1: return to tail
+            p = blk.live.popleft()
+            blk.spec_vis[blk.frame_of.pop(p)] = kept
+            blk.free.append(p)                     # reading R1: return to tail
             moved += 1
         if moved:
             blk.last = None                        # reading R11
@@ -282,18 +334,23 @@ class PagePoolOracle:
         """evict_frames(block_idx, scale_frames, sliding_window, ...).
 
         [LB-KV] "Append and Evict API" / "Streaming Forward Pass".  Scale pages
-        and the special stream are never evicted ([LB-SLOT] "scale frames" and
-        "特殊 token 流").  While eviction is deferred this is a no-op
-        ([LB-PERF] "Deferred Eviction Strategy").  Only the default flag values
-        are supported (reading R13).  Returns the number of pages moved.
+        and the special stream's bytes are never evicted ([LB-SLOT] "scale
+        frames" and "特殊 token 流").  While eviction is deferred this moves
+        nothing ([LB-PERF] "Deferred Eviction Strategy").  The flags (each 0
+        or 1) say what of an evicted frame's special tokens stays visible
+        (special_tokens_kept); the block records them, and a later
+        execute_deferred_eviction, which takes none, uses them (reading R13).
+        Returns the number of pages moved.
         """
         self._check_block(b)
-        if cross_frame_special != 1 or camera_only != 0:
-            raise OracleError("UNSUPPORTED")
+        if cross_frame_special not in (0, 1) or camera_only not in (0, 1):
+            raise OracleError("INVALID_ARG")
         self._check_evict_args(scale_frames, sliding_window)
+        blk = self.blocks[b]
+        blk.flags = (cross_frame_special, camera_only)
         if self.defer:
             return 0
-        return self._evict_to(self.blocks[b], sliding_window)
+        return self._evict_to(blk, sliding_window)
 
     def set_defer_eviction(self, enable):
         """_set_defer_eviction(True/False) ([LB-SLOT] "进阶：光流关键帧与回滚机制";
@@ -303,7 +360,8 @@ class PagePoolOracle:
     def execute_deferred_eviction(self, b, scale_frames, sliding_window):
         """execute_deferred_eviction(block_idx, scale_frames, sliding_window):
         perform the eviction that deferral held back, whatever the flag says
-        ([LB-SLOT] "进阶：光流关键帧与回滚机制")."""
+        ([LB-SLOT] "进阶：光流关键帧与回滚机制"), with the special-token flags of
+        the block's last evict_frames call (reading R13)."""
         self._check_block(b)
         self._check_evict_args(scale_frames, sliding_window)
         return self._evict_to(self.blocks[b], sliding_window)
@@ -325,6 +383,8 @@ class PagePoolOracle:
         assert lst[-1] == p
         lst.pop()
         blk.free.appendleft(p)          # reading R1: back to the head
+        del blk.frame_of[p]
+        blk.spec_vis.pop()
         blk.nsf -= 1
         blk.last = None
         return p
@@ -346,6 +406,9 @@ class PagePoolOracle:
         Indexing": last_page_len is the number of valid tokens in the final,
         possibly partly filled, special page.  [LB-PERF] "One-Time Planning
         Pattern": built once on block 0 and reused by every block.
+        Special pages none of whose tokens is visible any more (reading R13)
+        are left out of the table; the newest frame is always resident, so the
+        stream's last page, the one last_page_len describes, always stays.
         """
         c = self.cfg
         blk = self.blocks[0]
@@ -353,7 +416,9 @@ class PagePoolOracle:
             raise OracleError("EMPTY")
         fpp = c.frames_per_special_page
         n_sp = -(-blk.nsf // fpp)
-        specials = [c.num_patch_pages + i for i in range(n_sp)]
+        specials = [c.num_patch_pages + i for i in range(n_sp)
+                    if any(blk.spec_vis[i * fpp:(i + 1) * fpp])]
+        assert specials[-1] == c.num_patch_pages + n_sp - 1
         table = list(blk.scale) + list(blk.live) + specials
         last_page_len = c.num_special_tokens * (blk.nsf - fpp * (n_sp - 1))
         self.plan_state = Plan(
@@ -363,6 +428,7 @@ class PagePoolOracle:
             scale=tuple(blk.scale),
             live=tuple(blk.live),
             nsf=blk.nsf,
+            spec_vis=tuple(blk.spec_vis),
         )
         return self.plan_state
 
@@ -375,7 +441,7 @@ class PagePoolOracle:
             raise OracleError("NOT_PLANNED")
         blk = self.blocks[b]
         if (tuple(blk.scale) != pl.scale or tuple(blk.live) != pl.live
-                or blk.nsf != pl.nsf):
+                or blk.nsf != pl.nsf or tuple(blk.spec_vis) != pl.spec_vis):
             raise OracleError("STALE_PLAN")
         return pl
 
@@ -393,18 +459,41 @@ class PagePoolOracle:
         blk = self.blocks[b]
         return list(blk.scale), list(blk.live), list(blk.free), blk.nsf
 
+    def special_visibility(self, b):
+        """Block b's spec_vis as runs [first frame, frames, visible tokens per
+        frame] of equal counts, frames with none left out."""
+        self._check_block(b)
+        return special_runs(self.blocks[b].spec_vis)
 
-def visible_tokens_closed_form(cfg, committed, own=False):
+
+def special_runs(spec_vis):
+    """A per-frame visible-special count list as runs of equal counts:
+    [first frame, number of frames, count], runs with count 0 omitted."""
+    runs = []
+    for f, n in enumerate(spec_vis):
+        if runs and runs[-1][2] == n and runs[-1][0] + runs[-1][1] == f:
+            runs[-1][1] += 1
+        elif n:
+            runs.append([f, 1, n])
+    return runs
+
+
+def visible_tokens_closed_form(cfg, committed, own=False, kept=None):
     """Visible valid tokens after `committed` frames are in the cache and
     evicted to the window, plus an optional own (pending) frame.
 
     Follows from the routing and window rules: the first S frames stay, at
-    most W later ones are live, every frame keeps its special tokens.
+    most W later ones are live; a frame whose patch page is held keeps its
+    special tokens, an evicted one keeps ``kept`` of them (all by default,
+    reading R13).
     """
     s, w = cfg.scale_frames, cfg.sliding_window
     k = committed
+    if kept is None:
+        kept = cfg.num_special_tokens
     n_patch_frames = min(k, s) + min(max(k - s, 0), w)
-    n = cfg.patch_tokens * n_patch_frames + cfg.num_special_tokens * k
+    n = (cfg.patch_tokens + cfg.num_special_tokens) * n_patch_frames
+    n += kept * (k - n_patch_frames)
     if own:
         n += cfg.patch_tokens + cfg.num_special_tokens
     return n
@@ -423,5 +512,6 @@ def ceil_div(a, b):
 
 __all__ = [
     "ERRORS", "OracleError", "OracleConfig", "Plan", "PagePoolOracle",
-    "visible_tokens_closed_form", "window_mode_frames", "ceil_div",
+    "special_tokens_kept", "special_runs", "visible_tokens_closed_form",
+    "window_mode_frames", "ceil_div",
 ]

@@ -30,17 +30,21 @@ def rand_bits(rng, shape, scale=1.0):
     return f64_to_bf16_bits(rng.standard_normal(shape) * scale)
 
 
-def run_stream(cfg, schedule, seed, sm_scale=0.125):
+def run_stream(cfg, schedule, seed, sm_scale=0.125, flags=(1, 0)):
     """Drive the page-pool oracle and the brute-force model side by side.
 
     schedule: list of 'key' (append + evict, committed), 'transient' (defer,
     append, attend, rollback), 'accept'/'reject' (append under deferral,
-    attend, then execute / rollback), 'reset'.
+    attend, then execute / rollback), 'reset'.  Every evict_frames call
+    passes `flags` (cross_frame_special, camera_only); the brute-force model
+    keeps as many specials of a frame past the window as those flags say.
     Returns the number of attention comparisons made.
     """
     rng = np.random.default_rng(seed)
     o = PagePoolOracle(cfg, track_pool=[0])
-    bf = BruteForceStream(cfg.scale_frames, cfg.sliding_window, cfg.num_special_tokens)
+    kept = 0 if not flags[0] else 1 if flags[1] else cfg.num_special_tokens
+    bf = BruteForceStream(cfg.scale_frames, cfg.sliding_window, cfg.num_special_tokens,
+                          kept=kept)
     t, h, d = cfg.tokens_per_frame, cfg.num_heads, cfg.head_dim
     n_cmp = 0
     for ev in schedule:
@@ -56,7 +60,7 @@ def run_stream(cfg, schedule, seed, sm_scale=0.125):
                 o.append_frame(0, k, v)
             except OracleError:
                 return n_cmp
-            o.evict_frames(0, cfg.scale_frames, cfg.sliding_window)
+            o.evict_frames(0, cfg.scale_frames, cfg.sliding_window, *flags)
             bf.commit(bf16_bits_to_f64(k), bf16_bits_to_f64(v))
             own = (None, None)
         else:
@@ -76,7 +80,7 @@ def run_stream(cfg, schedule, seed, sm_scale=0.125):
             except OracleError:
                 o.set_defer_eviction(False)
                 return n_cmp
-            o.evict_frames(0, cfg.scale_frames, cfg.sliding_window)  # no-op
+            o.evict_frames(0, cfg.scale_frames, cfg.sliding_window, *flags)  # no-op
             own = (bf16_bits_to_f64(k), bf16_bits_to_f64(v))
         pl = o.plan()
         o.check_run(0)
@@ -132,10 +136,31 @@ def test_brute_force_padded_pages_and_odd_sizes():
 @settings(max_examples=60, deadline=None)
 @given(sched=st.lists(st.sampled_from(["key", "transient", "accept", "reject", "reset"]),
                       min_size=1, max_size=25),
-       s=st.integers(0, 3), w=st.integers(1, 4), seed=st.integers(0, 1000))
-def test_brute_force_random_schedules(sched, s, w, seed):
+       s=st.integers(0, 3), w=st.integers(1, 4), seed=st.integers(0, 1000),
+       flags=st.sampled_from([(1, 0), (1, 1), (0, 0), (0, 1)]))
+def test_brute_force_random_schedules(sched, s, w, seed, flags):
     c = OracleConfig(1, 2, 4, 9, 7, 3, s, w, 2, 40)
-    run_stream(c, sched, seed)
+    run_stream(c, sched, seed, flags=flags)
+
+
+EVICTION_FLAGS = [(1, 1), (0, 0), (0, 1)]
+
+
+@pytest.mark.parametrize("flags", EVICTION_FLAGS)
+def test_brute_force_eviction_flags(flags):
+    """Parts 1+2 against the page-free model when evicted frames keep only
+    their camera token or none of their specials (reading R13): keyframes,
+    interval two, accept/reject under deferral (execute_deferred_eviction
+    takes the flags of the deferred evict_frames call) and resets."""
+    assert run_stream(TINY, ["key"] * 12, 11, flags=flags) == 12
+    assert run_stream(TINY, ["key", "transient"] * 8, 12, flags=flags) == 16
+    rng = np.random.default_rng(13)
+    sched = ["accept" if rng.random() < 0.4 else "reject" for _ in range(30)]
+    assert run_stream(TINY, sched, 13, flags=flags) == 30
+    sched = ["key"] * 9 + ["reset"] + ["key", "transient"] * 6
+    assert run_stream(TINY, sched, 14, flags=flags) == 21
+    c2 = OracleConfig(1, 2, 4, 13, 11, 4, 1, 2, 1, 20)
+    assert run_stream(c2, ["key"] * 9 + ["transient", "accept"] * 4, 15, flags=flags) == 17
 
 
 # --------------------------------------------------- attention special cases

@@ -49,6 +49,8 @@ def _pin_suite(golden_dir):
         tb.test_widening_signed_zero_and_infinities,
         tb.test_widening_every_pattern_matches_torch,
         lambda: [tb.test_narrowing_rounds_to_nearest_even(x, b) for x, b in tb.NARROW],
+        lambda: tp.test_eviction_flags_worked_example(golden_dir),
+        lambda: [ta.test_brute_force_eviction_flags(f) for f in ta.EVICTION_FLAGS],
     ]
 
 
@@ -269,6 +271,52 @@ def _m17(mp):
         u = f.view(np.uint32).astype(np.uint64)
         return ((u + np.uint64(0x8000)) >> np.uint64(16)).astype(np.uint16)
     mp.setattr(bf, "f64_to_bf16_bits", narrow)
+
+
+@mutant("camera token taken as the last of a frame's specials")
+def _m18(mp):
+    def visible_slots(self, cfg):
+        ns, fpp, m = cfg.num_special_tokens, cfg.frames_per_special_page, cfg.num_patch_pages
+        out = []
+        for i, (page, n) in enumerate(zip(self.table, self.page_lengths(cfg))):
+            if i < self.n_patch:
+                out.append(list(range(n)))
+                continue
+            out.append([o for o in range(n)
+                        if o % ns >= ns - self.spec_vis[(page - m) * fpp + o // ns]])
+        return out
+    mp.setattr(pp.Plan, "visible_slots", visible_slots)
+
+
+@mutant("evicted frames keep every special whatever the flags")
+def _m19(mp):
+    mp.setattr(pp, "special_tokens_kept", lambda cfg, cross, camera: cfg.num_special_tokens)
+
+
+@mutant("a deferred evict_frames call does not record its flags")
+def _m20(mp):
+    orig = pp.PagePoolOracle.evict_frames
+
+    def evict(self, b, s, w, cross_frame_special=1, camera_only=0):
+        if self.defer:
+            self._check_block(b)
+            self._check_evict_args(s, w)
+            return 0
+        return orig(self, b, s, w, cross_frame_special, camera_only)
+    mp.setattr(pp.PagePoolOracle, "evict_frames", evict)
+
+
+@mutant("special pages with no visible token stay in the table")
+def _m21(mp):
+    orig = pp.PagePoolOracle.plan
+
+    def plan(self):
+        pl = orig(self)
+        c = self.cfg
+        n_sp = -(-pl.nsf // c.frames_per_special_page)
+        pl.table = pl.table[:pl.n_patch] + [c.num_patch_pages + i for i in range(n_sp)]
+        return pl
+    mp.setattr(pp.PagePoolOracle, "plan", plan)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
 
+import oracle.pagepool as pp
 from oracle import OracleConfig, OracleError, PagePoolOracle
 from oracle.pagepool import visible_tokens_closed_form, window_mode_frames
 
@@ -142,6 +143,74 @@ def test_tiny_stream_worked_example(golden_dir):
     o.rollback_last_frame(0)
     scale, live, free, nsf = o.block_state(0)
     assert free == rp["after_free"] and live == rp["after_live"] and nsf == rp["after_nsf"]
+
+
+def _flag_schedule(sc):
+    """Per-frame eviction flags of a scenario: the first entry's flags for
+    its count of frames, then one frame each for the entries of `then`."""
+    flags, n = sc["flags"]
+    return [tuple(flags)] * n + [tuple(f) for f in sc.get("then", [])]
+
+
+def test_eviction_flags_worked_example(golden_dir):
+    """Hand-derived tables, special runs and visible counts under each pair of
+    eviction flags, a change of flags mid-stream and a deferred eviction that
+    takes the flags of the deferred call (reading R13)."""
+    g = load(golden_dir, "eviction_flags_tiny.json")
+    c = OracleConfig(**g["config"])
+    for sc in g["scenarios"]:
+        o = PagePoolOracle(c)
+        checks = {row["t"]: row for row in sc["checks"]}
+        for t, flags in enumerate(_flag_schedule(sc)):
+            o.append_frame(0)
+            o.evict_frames(0, c.scale_frames, c.sliding_window, *flags)
+            pl = o.plan()
+            assert o.special_visibility(0) == pp.special_runs(pl.spec_vis)
+            if t in checks:
+                row = checks[t]
+                assert pl.table == row["table"], (sc["name"], t)
+                assert pl.last_page_len == row["last_page_len"]
+                assert o.special_visibility(0) == row["specials"], (sc["name"], t)
+                assert pl.num_visible_tokens(c) == row["nk"], (sc["name"], t)
+        d = sc.get("deferred")
+        if d:
+            o.set_defer_eviction(True)
+            o.append_frame(0)
+            assert o.evict_frames(0, c.scale_frames, c.sliding_window, 0, 0) == 0
+            assert o.execute_deferred_eviction(0, c.scale_frames, c.sliding_window) == 1
+            o.set_defer_eviction(False)
+            pl = o.plan()
+            assert pl.table == d["table"]
+            assert pl.last_page_len == d["last_page_len"]
+            assert o.special_visibility(0) == d["specials"]
+            assert pl.num_visible_tokens(c) == d["nk"]
+            assert o.block_state(0)[2] == d["free"]
+            o.reset()                      # a reset restores the default flags
+            assert o.blocks[0].flags == (1, 0)
+
+
+@settings(max_examples=100, deadline=None)
+@given(cfg=st.builds(
+    lambda ns, s, w, r: OracleConfig(1, 1, 1, 2 * ns + 1, 2 * ns, ns, s, w, r, 60),
+    ns=st.integers(1, 6), s=st.integers(0, 3), w=st.integers(1, 5), r=st.integers(1, 2)),
+    n=st.integers(1, 40), cross=st.integers(0, 1), camera=st.integers(0, 1))
+def test_closed_form_visible_tokens_under_eviction_flags(cfg, n, cross, camera):
+    """Nk = (P + 6) x held frames + kept x evicted frames, kept = 6, 1 or 0
+    for the flags; the special runs say the same frame by frame."""
+    o = PagePoolOracle(cfg)
+    kept = pp.special_tokens_kept(cfg, cross, camera)
+    assert kept == (0 if not cross else 1 if camera else cfg.num_special_tokens)
+    for k in range(1, n + 1):
+        o.append_frame(0)
+        o.evict_frames(0, cfg.scale_frames, cfg.sliding_window, cross, camera)
+        pl = o.plan()
+        assert pl.num_visible_tokens(cfg) == pp.visible_tokens_closed_form(cfg, k, kept=kept)
+        held = min(k, cfg.scale_frames) + min(max(k - cfg.scale_frames, 0), cfg.sliding_window)
+        evicted = k - held
+        assert sum(r[1] * r[2] for r in o.special_visibility(0)) == \
+            cfg.num_special_tokens * held + kept * evicted
+        # stats keep counting the stored specials: the stream's bytes stay
+        assert o.get_cache_stats(0)[4] == cfg.num_special_tokens * k
 
 
 # ------------------------------------------------------------- closed forms
@@ -292,10 +361,13 @@ def test_errors_and_strong_guarantee():
         o.append_frame(2)
     with pytest.raises(OracleError, match="NOTHING_TO_ROLLBACK"):
         o.rollback_last_frame(0)
-    with pytest.raises(OracleError, match="UNSUPPORTED"):
-        o.evict_frames(0, 1, 1, cross_frame_special=0)
-    with pytest.raises(OracleError, match="UNSUPPORTED"):
-        o.evict_frames(0, 1, 1, camera_only=1)
+    with pytest.raises(OracleError, match="INVALID_ARG"):
+        o.evict_frames(0, 1, 1, cross_frame_special=2)
+    with pytest.raises(OracleError, match="INVALID_ARG"):
+        o.evict_frames(0, 1, 1, camera_only=-1)
+    with pytest.raises(OracleError, match="INVALID_ARG"):
+        o.evict_frames(0, 1, 2, cross_frame_special=0)   # flags recorded only if valid
+    assert o.blocks[0].flags == (1, 0)
     with pytest.raises(OracleError, match="INVALID_ARG"):
         o.evict_frames(0, 2, 1)
     with pytest.raises(OracleError, match="INVALID_ARG"):
