@@ -152,10 +152,20 @@ SPKV_API int spkv_append_frame(spkv_handle* h, int32_t block, const void* k,
 /* evict_frames(block_idx, scale_frames, sliding_window, cross_frame_special,
  * camera_only) ([LB-KV] "Append and Evict API", "Streaming Forward Pass").
  * While the live window holds more than sliding_window pages, its oldest page
- * returns to the tail of the free list.  A no-op while eviction is deferred.
- * scale_frames must equal the config's; 1 <= sliding_window <= M - S.
- * Only cross_frame_special = 1 and camera_only = 0 are supported (the pages
- * name these flags but do not define the others): UNSUPPORTED otherwise. */
+ * returns to the tail of the free list.  Moves nothing while eviction is
+ * deferred.  scale_frames must equal the config's; 1 <= sliding_window <=
+ * M - S; each flag is 0 or 1 (else INVALID_ARG).
+ * The flags say what of an evicted frame's special tokens stays visible
+ * ([LB-KV] "Append and Evict API": specials are optionally preserved;
+ * [LB-SLOT] "特殊 token 流": preserved specials, camera tokens above all,
+ * carry context across frames): cross_frame_special = 1 keeps all of them
+ * (camera_only = 0, the default) or only the camera token, the first of the
+ * frame's specials (camera_only = 1); cross_frame_special = 0 keeps none.
+ * Frames whose patch page is held (scale pages, live window) show all their
+ * specials.  The special stream's bytes never change.  The block records the
+ * flags: they also govern the pages its next execute_deferred_eviction
+ * moves.  Special pages left with no visible token drop out of the plan's
+ * table; spkv_get_plan_specials describes the visible special tokens. */
 SPKV_API int spkv_evict_frames(spkv_handle* h, int32_t block,
                                int32_t scale_frames, int32_t sliding_window,
                                int32_t cross_frame_special,
@@ -166,7 +176,9 @@ SPKV_API int spkv_evict_frames(spkv_handle* h, int32_t block,
 SPKV_API int spkv_set_defer_eviction(spkv_handle* h, int32_t enable);
 
 /* execute_deferred_eviction(block_idx, scale_frames, sliding_window): the
- * eviction loop of evict_frames, run whatever the defer flag says. */
+ * eviction loop of evict_frames, run whatever the defer flag says, with the
+ * special-token flags of the block's last evict_frames call (the defaults
+ * 1, 0 before any since create or reset). */
 SPKV_API int spkv_execute_deferred_eviction(spkv_handle* h, int32_t block,
                                             int32_t scale_frames,
                                             int32_t sliding_window);
@@ -306,6 +318,20 @@ SPKV_API int spkv_get_cache_stats(const spkv_handle* h, int32_t block,
 SPKV_API int spkv_get_plan(const spkv_handle* h, int32_t* table, int32_t cap,
                            int32_t* n_pages, int32_t* n_patch_pages,
                            int32_t* last_page_len);
+
+/* The special tokens the current plan shows, as runs (3 int32 each: first
+ * frame of the special stream, number of frames, visible tokens per frame --
+ * the first that many of each frame's specials), in stream order, equal
+ * neighbours merged and runs with none left out; cap runs available.  The
+ * run() token order is the patch pages' tokens, then these.  NOT_PLANNED if
+ * there is no plan; INVALID_ARG if cap is too small. */
+SPKV_API int spkv_get_plan_specials(const spkv_handle* h, int32_t* runs, int32_t cap,
+                                    int32_t* n_runs);
+
+/* The same runs for block `block`'s current state (what a plan built from it
+ * would show), for inspection. */
+SPKV_API int spkv_get_block_specials(const spkv_handle* h, int32_t block, int32_t* runs,
+                                     int32_t cap, int32_t* n_runs);
 
 /* A block's allocator state, for inspection: scale list, live window (oldest
  * first), free list (head first), each into an array of cap entries, and

@@ -54,7 +54,8 @@ EXPORTED = (
     "spkv_execute_deferred_eviction", "spkv_rollback_last_frame", "spkv_reset",
     "spkv_plan", "spkv_run", "spkv_run_noalloc", "spkv_run_own", "spkv_run_batch", "spkv_set_num_splits",
     "spkv_get_cache_stats",
-    "spkv_get_plan", "spkv_get_block_state", "spkv_error_string",
+    "spkv_get_plan", "spkv_get_plan_specials", "spkv_get_block_specials",
+    "spkv_get_block_state", "spkv_error_string",
 )
 
 
@@ -124,6 +125,8 @@ def load_library(path=None):
         "spkv_set_num_splits": [vp, i32],
         "spkv_get_cache_stats": [vp, i32, ctypes.POINTER(Stats)],
         "spkv_get_plan": [vp, pi32, i32, pi32, pi32, pi32],
+        "spkv_get_plan_specials": [vp, pi32, i32, pi32],
+        "spkv_get_block_specials": [vp, i32, pi32, i32, pi32],
         "spkv_get_block_state": [vp, i32, pi32, pi32, pi32, i32, pi32, pi32,
                                  pi32, pi64],
     }
@@ -383,6 +386,23 @@ class PagedKVCache:
                                       ctypes.byref(npatch), ctypes.byref(lpl)),
                "spkv_get_plan")
         return list(tab[:n.value]), npatch.value, lpl.value
+
+    def _specials(self, fn, name, *args):
+        n = ctypes.c_int32()
+        _check(fn(self._h, *args, None, 0, ctypes.byref(n)), name)
+        buf = (ctypes.c_int32 * max(1, 3 * n.value))()
+        _check(fn(self._h, *args, buf, n.value, ctypes.byref(n)), name)
+        return [list(buf[3 * i:3 * i + 3]) for i in range(n.value)]
+
+    def get_plan_specials(self):
+        """The plan's visible special tokens: [first frame, frames, tokens
+        per frame] runs in stream order."""
+        return self._specials(self.lib.spkv_get_plan_specials, "spkv_get_plan_specials")
+
+    def get_block_specials(self, block):
+        """The same runs for a block's current state."""
+        return self._specials(self.lib.spkv_get_block_specials, "spkv_get_block_specials",
+                              block)
 
     def get_block_state(self, block):
         cap = self.max_num_pages

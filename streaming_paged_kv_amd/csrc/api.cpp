@@ -52,7 +52,7 @@ bool to_geometry(const spkv_config* c, spkv::Geometry* g) {
 }
 
 struct Sizes {
-  int64_t max_num_pages, pool_bytes, table_bytes, rowmap_entries,
+  int64_t max_num_pages, pool_bytes, table_bytes, segs_offset, rowmap_entries,
       rowmap_bytes, rowmap_own_bytes, min_ws;
 };
 
@@ -68,7 +68,12 @@ Sizes sizes_of(const spkv::Geometry& g) {
   s.max_num_pages = g.max_num_pages;
   s.pool_bytes = int64_t(g.max_num_pages) * 2 * g.page_size * g.num_heads *
                  g.head_dim * 2;
-  s.table_bytes = round_up(int64_t(g.max_num_pages) * 4, kAlign);
+  // A plan's device table: the page ids, then (16-byte aligned) the runs of
+  // visible special tokens, at most one per evicted run plus two.
+  s.segs_offset = round_up(int64_t(g.max_num_pages) * 4, 16);
+  s.table_bytes = round_up(s.segs_offset + (g.special_capacity + 2) *
+                                               int64_t(sizeof(spkv::SpecialSeg)),
+                           kAlign);
   // Row map: at most every slot of every page is visible; rounded up to a
   // key tile and padded.
   s.rowmap_entries = round_up(int64_t(g.max_num_pages) * g.page_size,
@@ -118,7 +123,7 @@ struct spkv_handle {
   int32_t* dev_table[2] = {nullptr, nullptr};
   uint32_t* dev_rowmap[2] = {nullptr, nullptr};
   uint32_t* dev_rowmap_own[2] = {nullptr, nullptr};
-  int32_t* stage = nullptr;          // pinned, 2 x max_num_pages
+  char* stage = nullptr;             // pinned, 2 x table_bytes
   hipEvent_t copied[2] = {nullptr, nullptr};
   bool copy_pending[2] = {false, false};
   int plan_slot = 0;                 // slot holding the current plan
@@ -229,8 +234,7 @@ SPKV_API int spkv_create(const spkv_config* cfg, void* const* pool_ptrs,
   void* scratch = nullptr;
   if (spkv::scratch_address(&scratch) != hipSuccess) return SPKV_ERR_HIP;
   h->scratch = static_cast<char*>(scratch);
-  if (hipHostMalloc(reinterpret_cast<void**>(&h->stage),
-                    size_t(2) * g.max_num_pages * sizeof(int32_t),
+  if (hipHostMalloc(reinterpret_cast<void**>(&h->stage), size_t(2 * sz.table_bytes),
                     hipHostMallocDefault) != hipSuccess) {
     h->stage = nullptr;
     return SPKV_ERR_HIP;
@@ -346,18 +350,30 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream) {
   const spkv::Status s = h->pool->build_plan();
   if (s != spkv::Status::ok) return status(s);
   const spkv::PlanView pv = h->pool->pending_view();
-  int32_t* host = h->stage + size_t(slot) * h->g.max_num_pages;
+  const Sizes& sz = h->sz;
+  char* host = h->stage + slot * sz.table_bytes;
   std::memcpy(host, pv.table, size_t(pv.n_pages) * sizeof(int32_t));
+  spkv::SpecialSeg* segs = reinterpret_cast<spkv::SpecialSeg*>(host + sz.segs_offset);
+  int32_t offset = 0;
+  for (int32_t i = 0; i < pv.n_segs; ++i) {
+    const spkv::SpecialRun& r = pv.segs[i];
+    segs[i] = spkv::SpecialSeg{r.first, r.count, r.kept, offset};
+    offset += r.count * r.kept;
+  }
+  const size_t bytes = size_t(sz.segs_offset) + size_t(pv.n_segs) * sizeof(spkv::SpecialSeg);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const spkv::Geometry& g = h->g;
+  char* dev = reinterpret_cast<char*>(h->dev_table[slot]);
   spkv::PlanArgs pa;
   pa.table = h->dev_table[slot];
+  pa.segs = reinterpret_cast<const spkv::SpecialSeg*>(dev + sz.segs_offset);
   pa.rowmap = h->dev_rowmap[slot];
   pa.n_patch = pv.n_patch;
-  pa.n_pages = pv.n_pages;
+  pa.n_segs = pv.n_segs;
   pa.patch_len = g.patch_tokens;
-  pa.special_len = g.num_special * g.frames_per_spage;
-  pa.last_len = pv.last_page_len;
+  pa.num_special = g.num_special;
+  pa.frames_per_spage = g.frames_per_spage;
+  pa.first_spage = g.num_patch_pages;
   pa.page_size = g.page_size;
   pa.nk = static_cast<int32_t>(pv.visible_tokens);
   pa.n_out = static_cast<int32_t>(
@@ -367,8 +383,7 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream) {
   pa.n_out_own = static_cast<int32_t>(
       round_up(pv.visible_tokens + g.tokens_per_frame, spkv::kAttnKeyTile) +
       spkv::kRowmapPad);
-  if (hipMemcpyAsync(h->dev_table[slot], host, size_t(pv.n_pages) * sizeof(int32_t),
-                     hipMemcpyHostToDevice, st) != hipSuccess ||
+  if (hipMemcpyAsync(dev, host, bytes, hipMemcpyHostToDevice, st) != hipSuccess ||
       hipEventRecord(h->copied[slot], st) != hipSuccess ||
       spkv::launch_expand(pa, st) != hipSuccess) {
     return SPKV_ERR_HIP;  // the pending plan is simply not committed
@@ -652,6 +667,44 @@ SPKV_API int spkv_get_plan(const spkv_handle* h, int32_t* table, int32_t cap,
   if (n_patch_pages) *n_patch_pages = pv.n_patch;
   if (last_page_len) *last_page_len = pv.last_page_len;
   return SPKV_OK;
+}
+
+namespace {
+
+int copy_specials(const spkv::SpecialRun* runs, int32_t n, int32_t* out, int32_t cap,
+                  int32_t* n_runs) {
+  if (out) {
+    if (cap < n) return SPKV_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < n; ++i) {
+      out[3 * i + 0] = runs[i].first;
+      out[3 * i + 1] = runs[i].count;
+      out[3 * i + 2] = runs[i].kept;
+    }
+  }
+  if (n_runs) *n_runs = n;
+  return SPKV_OK;
+}
+
+}  // namespace
+
+SPKV_API int spkv_get_plan_specials(const spkv_handle* h, int32_t* runs, int32_t cap,
+                                    int32_t* n_runs) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  if (!h->pool->planned()) return SPKV_ERR_NOT_PLANNED;
+  const spkv::PlanView pv = h->pool->plan_view();
+  return copy_specials(pv.segs, pv.n_segs, runs, cap, n_runs);
+}
+
+SPKV_API int spkv_get_block_specials(const spkv_handle* h, int32_t block, int32_t* runs,
+                                     int32_t cap, int32_t* n_runs) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  int32_t n = 0;
+  spkv::Status s = h->pool->block_specials(block, nullptr, 0, &n);
+  if (s != spkv::Status::ok) return status(s);
+  std::vector<spkv::SpecialRun> tmp(n);   // inspection only
+  s = h->pool->block_specials(block, tmp.data(), n, &n);
+  if (s != spkv::Status::ok) return status(s);
+  return copy_specials(tmp.data(), n, runs, cap, n_runs);
 }
 
 SPKV_API int spkv_get_block_state(const spkv_handle* h, int32_t block,

@@ -81,21 +81,31 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSumLimit = 65536.0f;   // bound on a lane's partial row sum
 
 // ------------------------------------------------------------- plan expand
-// Pool row of visible token t (0 <= t < nk) of a plan.
+// Pool row of visible token t (0 <= t < nk) of a plan: the patch pages'
+// tokens in table order, then the visible special tokens run by run (frame f
+// of the special stream sits in page first_spage + f / frames_per_spage at
+// slot num_special * (f % frames_per_spage)).
 __device__ __forceinline__ uint32_t plan_row(const PlanArgs& p, int t) {
   const int patch_tokens = p.n_patch * p.patch_len;
-  int e, o;
   if (t < patch_tokens) {
-    e = t / p.patch_len;
-    o = t - e * p.patch_len;
-  } else {
-    const int u = t - patch_tokens;
-    const int k = u / p.special_len;
-    e = p.n_patch + k;
-    o = u - k * p.special_len;
+    const int e = t / p.patch_len;
+    return static_cast<uint32_t>(p.table[e]) * 2u * static_cast<uint32_t>(p.page_size) +
+           static_cast<uint32_t>(t - e * p.patch_len);
   }
-  return static_cast<uint32_t>(p.table[e]) * 2u * static_cast<uint32_t>(p.page_size) +
-         static_cast<uint32_t>(o);
+  const int u = t - patch_tokens;
+  int lo = 0, hi = p.n_segs - 1;   // last run with offset <= u
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.segs[mid].offset <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  const SpecialSeg s = p.segs[lo];
+  const int r = u - s.offset;
+  const int f = s.first + r / s.kept;
+  const int page = p.first_spage + f / p.frames_per_spage;
+  const int slot = p.num_special * (f % p.frames_per_spage) + r % s.kept;
+  return static_cast<uint32_t>(page) * 2u * static_cast<uint32_t>(p.page_size) +
+         static_cast<uint32_t>(slot);
 }
 
 __global__ __launch_bounds__(256) void expand_kernel(PlanArgs p) {

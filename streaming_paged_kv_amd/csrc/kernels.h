@@ -33,16 +33,24 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // repeat the last of these.
 constexpr uint32_t kOwnRow = 0x80000000u;
 
+// A run of frames of the special stream whose first `kept` special tokens
+// are visible; `offset` counts the visible special tokens before it.
+struct SpecialSeg {
+  int32_t first, count, kept, offset;
+};
+
 struct PlanArgs {
-  const int32_t* table;     // device page table, n_pages entries
+  const int32_t* table;     // device page table, n_patch patch entries used
+  const SpecialSeg* segs;   // device, n_segs runs in stream order
   uint32_t* rowmap;         // out: n_out entries
   uint32_t* rowmap_own;     // out: n_out_own entries
   int32_t n_own;            // rows of a frame (specials + patches)
   int32_t n_out_own;        // entries written to rowmap_own
-  int32_t n_patch, n_pages;
+  int32_t n_patch, n_segs;
   int32_t patch_len;        // valid tokens of a patch page
-  int32_t special_len;      // valid tokens of a full special page
-  int32_t last_len;         // valid tokens of the last special page
+  int32_t num_special;      // special tokens of a frame
+  int32_t frames_per_spage; // frames of a special page
+  int32_t first_spage;      // page id of the special stream's first page
   int32_t page_size;
   int32_t nk;               // visible tokens
   int32_t n_out;            // entries written (nk rounded up, plus padding)

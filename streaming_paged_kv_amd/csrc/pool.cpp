@@ -43,8 +43,10 @@ PagePool::PagePool(const Geometry& g) : g_(g) {
 
 void PagePool::init_plan(PlanData& p) const {
   p.table.assign(g_.max_num_pages, 0);
+  p.segs.assign(max_special_segments(), SpecialRun{0, 0, 0});
   p.scale.reserve(g_.scale_frames);
   p.live.reserve(g_.num_patch_pages);
+  p.evicted.reserve(g_.special_capacity);
 }
 
 void PagePool::init_block(Block& b) {
@@ -57,6 +59,9 @@ void PagePool::init_block(Block& b) {
   b.nsf = 0;
   b.last_page = -1;
   b.last_in_scale = false;
+  b.evicted.clear();
+  b.evicted.reserve(g_.special_capacity);
+  b.kept_on_evict = g_.num_special;  // the pages' default flags (1, 0)
 }
 
 // [LB-KV] "Append and Evict API"; [LB-SLOT] "scale frames：永不驱逐的前 8 个
@@ -109,27 +114,46 @@ Status PagePool::check_evict_args(int32_t scale_frames, int32_t window) const {
 }
 
 // [LB-SLOT] "keyframes：滑动窗口 slot 的进出规则": when the window is over its
-// limit the oldest page goes back to the free list for reuse.
+// limit the oldest page goes back to the free list for reuse.  The frame it
+// held keeps kept_on_evict of its special tokens in view; their bytes stay.
 int32_t PagePool::evict_to(Block& b, int32_t window) {
   int32_t moved = 0;
   while (b.live.size() > window) {
+    // The live window holds frames nsf - live .. nsf - 1; the oldest leaves.
+    const int32_t f = static_cast<int32_t>(b.nsf) - b.live.size();
     b.free_list.push_back(b.live.pop_front());
+    SpecialRun* last = b.evicted.empty() ? nullptr : &b.evicted.back();
+    if (last && last->kept == b.kept_on_evict && last->first + last->count == f)
+      ++last->count;
+    else
+      b.evicted.push_back(SpecialRun{f, 1, b.kept_on_evict});
     ++moved;
   }
   if (moved) b.last_page = -1;  // the last append can no longer be undone
   return moved;
 }
 
+// [LB-KV] "Append and Evict API": eviction recycles the oldest patch pages,
+// optionally preserving special tokens; [LB-SLOT] "特殊 token 流": preserved
+// specials carry context across frames, the camera tokens in particular.
+// cross_frame_special = 1 keeps an evicted frame's specials in view (only
+// its camera token, the first, with camera_only = 1); 0 keeps none.  The
+// flags apply to the pages this call moves and, under deferral, to those the
+// block's next execute_deferred_eviction moves.
 Status PagePool::evict(int32_t block, int32_t scale_frames, int32_t window,
                        int32_t cross_frame_special, int32_t camera_only,
                        int32_t* moved) {
   if (!valid_block(block)) return Status::bad_block;
-  if (cross_frame_special != 1 || camera_only != 0) return Status::unsupported;
+  if ((cross_frame_special != 0 && cross_frame_special != 1) ||
+      (camera_only != 0 && camera_only != 1))
+    return Status::invalid_arg;
   Status s = check_evict_args(scale_frames, window);
   if (s != Status::ok) return s;
+  Block& b = blocks_[block];
+  b.kept_on_evict = cross_frame_special ? (camera_only ? 1 : g_.num_special) : 0;
   int32_t m = 0;
   // [LB-PERF] "Deferred Eviction Strategy": paused while deferred.
-  if (!defer_) m = evict_to(blocks_[block], window);
+  if (!defer_) m = evict_to(b, window);
   if (moved) *moved = m;
   return Status::ok;
 }
@@ -171,6 +195,30 @@ void PagePool::reset() {
 // [LB-KV] "Patch Pages vs. Special Pages" (scale -> live -> special) and
 // "Physical Page Layout and Indexing" (last_page_len); [LB-PERF] "One-Time
 // Planning Pattern" (block 0 only).
+// Frames 0 .. S-1 (the scale pages) and the live window's frames show all of
+// their specials; the evicted frames between them show their runs' counts.
+int32_t PagePool::special_segments(const Block& b, SpecialRun* out) const {
+  int32_t n = 0;
+  auto add = [&](int32_t first, int32_t count, int32_t kept) {
+    if (count <= 0 || kept <= 0) return;
+    if (n > 0 && out[n - 1].kept == kept && out[n - 1].first + out[n - 1].count == first)
+      out[n - 1].count += count;
+    else
+      out[n++] = SpecialRun{first, count, kept};
+  };
+  const int32_t nsf = static_cast<int32_t>(b.nsf);
+  const int32_t held_from = nsf - b.live.size();  // first frame of the window
+  int32_t f = 0;
+  if (!b.evicted.empty()) {
+    add(0, b.evicted.front().first, g_.num_special);
+    for (const SpecialRun& r : b.evicted) add(r.first, r.count, r.kept);
+    f = b.evicted.back().first + b.evicted.back().count;
+  }
+  add(f, held_from - f, g_.num_special);      // scale frames (no eviction yet)
+  add(held_from, nsf - held_from, g_.num_special);
+  return n;
+}
+
 Status PagePool::build_plan() {
   const Block& b = blocks_[0];
   if (b.nsf == 0) return Status::empty;
@@ -181,15 +229,28 @@ Status PagePool::build_plan() {
   for (int32_t x : b.scale) p.table[n++] = x;
   for (int32_t i = 0; i < b.live.size(); ++i) p.table[n++] = b.live[i];
   p.n_patch = n;
-  for (int32_t i = 0; i < n_sp; ++i) p.table[n++] = g_.num_patch_pages + i;
+  p.n_segs = special_segments(b, p.segs.data());
+  // Special pages that hold at least one visible token, in stream order.
+  int64_t special_tokens = 0;
+  int32_t last_sp = -1;
+  for (int32_t i = 0; i < p.n_segs; ++i) {
+    const SpecialRun& r = p.segs[i];
+    special_tokens += int64_t(r.count) * r.kept;
+    for (int32_t k = std::max(last_sp + 1, r.first / fpp);
+         k <= (r.first + r.count - 1) / fpp; ++k)
+      p.table[n++] = g_.num_patch_pages + k;
+    last_sp = (r.first + r.count - 1) / fpp;
+  }
   p.n_pages = n;
+  // The newest frame is always held, so the stream's last special page, the
+  // one last_page_len describes, is always the table's last entry.
   p.last_page_len =
       g_.num_special * static_cast<int32_t>(b.nsf - int64_t(fpp) * (n_sp - 1));
-  p.visible_tokens = int64_t(p.n_patch) * g_.patch_tokens +
-                     int64_t(n_sp - 1) * g_.num_special * fpp + p.last_page_len;
+  p.visible_tokens = int64_t(p.n_patch) * g_.patch_tokens + special_tokens;
   p.scale.assign(b.scale.begin(), b.scale.end());
   p.live.clear();
   for (int32_t i = 0; i < b.live.size(); ++i) p.live.push_back(b.live[i]);
+  p.evicted.assign(b.evicted.begin(), b.evicted.end());
   p.nsf = b.nsf;
   return Status::ok;
 }
@@ -218,6 +279,9 @@ Status PagePool::check_run(int32_t block) const {
     return Status::stale_plan;
   for (int32_t i = 0; i < b.live.size(); ++i)
     if (b.live[i] != cur_.live[i]) return Status::stale_plan;
+  if (b.evicted.size() != cur_.evicted.size() ||
+      !std::equal(b.evicted.begin(), b.evicted.end(), cur_.evicted.begin()))
+    return Status::stale_plan;
   return Status::ok;
 }
 
@@ -254,6 +318,19 @@ Status PagePool::block_state(int32_t block, int32_t* scale, int32_t* live,
   if (n_live) *n_live = b.live.size();
   if (n_free) *n_free = b.free_list.size();
   if (nsf) *nsf = b.nsf;
+  return Status::ok;
+}
+
+Status PagePool::block_specials(int32_t block, SpecialRun* out, int32_t cap,
+                                int32_t* n) const {
+  if (!valid_block(block)) return Status::bad_block;
+  const Block& b = blocks_[block];
+  // At most one segment per evicted run plus the two held ranges.
+  std::vector<SpecialRun> segs(b.evicted.size() + 2);  // inspection, not the hot path
+  const int32_t k = special_segments(b, segs.data());
+  if (out && cap < k) return Status::invalid_arg;
+  if (out) std::copy(segs.begin(), segs.begin() + k, out);
+  if (n) *n = k;
   return Status::ok;
 }
 

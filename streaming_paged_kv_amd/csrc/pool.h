@@ -97,12 +97,23 @@ struct AppendResult {
   bool prev_last_in_scale;
 };
 
+// Frames [first, first + count) of the special stream, each showing its
+// first `kept` special tokens to attention.
+struct SpecialRun {
+  int32_t first, count, kept;
+  bool operator==(const SpecialRun& o) const {
+    return first == o.first && count == o.count && kept == o.kept;
+  }
+};
+
 struct PlanView {
   const int32_t* table;
   int32_t n_pages;
   int32_t n_patch;
   int32_t last_page_len;
   int64_t visible_tokens;
+  const SpecialRun* segs;   // visible special tokens, in stream order
+  int32_t n_segs;
 };
 
 class PagePool {
@@ -143,6 +154,14 @@ class PagePool {
   Status block_state(int32_t block, int32_t* scale, int32_t* live,
                      int32_t* free_list, int32_t cap, int32_t* n_scale,
                      int32_t* n_live, int32_t* n_free, int64_t* nsf) const;
+  // The special tokens block `block` shows, as coalesced runs (the segments
+  // its plan would carry); *n gets the count, out (cap runs) the runs.
+  Status block_specials(int32_t block, SpecialRun* out, int32_t cap,
+                        int32_t* n) const;
+  // Runs a plan or a block can hold at most.
+  int32_t max_special_segments() const {
+    return static_cast<int32_t>(g_.special_capacity) + 2;
+  }
 
  private:
   struct Block {
@@ -152,11 +171,18 @@ class PagePool {
     int64_t nsf = 0;
     int32_t last_page = -1;      // -1: nothing to roll back
     bool last_in_scale = false;
+    // Evicted frames (a contiguous range starting at frame S, as eviction
+    // is first in, first out) as runs of equal kept counts; reserved to the
+    // special stream's capacity, never reallocates.
+    std::vector<SpecialRun> evicted;
+    int32_t kept_on_evict = 0;   // special tokens an evicted frame keeps
   };
   void init_block(Block& b);
   bool valid_block(int32_t b) const { return b >= 0 && b < g_.num_blocks; }
   Status check_evict_args(int32_t scale_frames, int32_t window) const;
   int32_t evict_to(Block& b, int32_t window);
+  // Visible special tokens of a block as coalesced runs (kept > 0 only).
+  int32_t special_segments(const Block& b, SpecialRun* out) const;
 
   Geometry g_;
   std::vector<Block> blocks_;
@@ -167,13 +193,16 @@ class PagePool {
     std::vector<int32_t> table;
     int32_t n_pages = 0, n_patch = 0, last_page_len = 0;
     int64_t visible_tokens = 0;
+    std::vector<SpecialRun> segs;  // capacity max_special_segments()
+    int32_t n_segs = 0;
     std::vector<int32_t> scale, live;
+    std::vector<SpecialRun> evicted;
     int64_t nsf = 0;
   };
   void init_plan(PlanData& p) const;
   static PlanView view_of(const PlanData& p) {
     return PlanView{p.table.data(), p.n_pages, p.n_patch, p.last_page_len,
-                    p.visible_tokens};
+                    p.visible_tokens, p.segs.data(), p.n_segs};
   }
   bool planned_ = false;
   PlanData cur_, next_;

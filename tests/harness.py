@@ -31,9 +31,10 @@ def frame_kinds(wl, frames=None):
     return out
 
 
-def gpu_step(cache, wl, kind, reset, qkv, outs, stream=None):
+def gpu_step(cache, wl, kind, reset, qkv, outs, stream=None, flags=(1, 0)):
     """One frame on the HIP side.  qkv[b] = (q, k, v) device tensors; the
-    run's output for block b is written into outs[b]."""
+    run's output for block b is written into outs[b]; evict_frames gets the
+    eviction flags (cross_frame_special, camera_only)."""
     S, W = wl.scale_frames, wl.sliding_window
     if reset:
         cache.reset()
@@ -44,7 +45,7 @@ def gpu_step(cache, wl, kind, reset, qkv, outs, stream=None):
     for b in range(wl.num_blocks):
         q, k, v = qkv[b]
         cache.append_frame(b, k, v, stream=stream)
-        cache.evict_frames(b, S, W)
+        cache.evict_frames(b, S, W, *flags)
         if b == 0:
             cache.plan(stream=stream)
         cache.run(b, q, out=outs[b], stream=stream)
@@ -57,7 +58,7 @@ def gpu_step(cache, wl, kind, reset, qkv, outs, stream=None):
         cache.set_defer_eviction(False)
 
 
-def dry_run(wl, frames=None):
+def dry_run(wl, frames=None, flags=(1, 0)):
     """State-machine-only pass over the schedule: for each frame, the plan
     (table, n_patch) and the frame that last wrote each page, plus
     milestone frames."""
@@ -77,7 +78,7 @@ def dry_run(wl, frames=None):
             o.set_defer_eviction(True)
         p, _, _ = o.append_frame(0)
         writer[p] = f
-        moved = o.evict_frames(0, wl.scale_frames, wl.sliding_window)
+        moved = o.evict_frames(0, wl.scale_frames, wl.sliding_window, *flags)
         pl = o.plan()
         plans.append((list(pl.table), pl.n_patch))
         writers_at.append(dict(writer))

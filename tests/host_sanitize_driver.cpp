@@ -7,9 +7,13 @@
 //   * the special stream never exceeds its physical capacity, and an append
 //     writes its specials at page M + f/fpp, slot 6*(f%fpp) for its frame f;
 //   * a call that returns an error leaves every block's state unchanged;
-//   * a plan lists scale, then live pages of block 0, then its special pages,
-//     with last_page_len = 6*(f - fpp*(n_sp-1)) and the visible token count
-//     that these imply; check_run accepts exactly the blocks in that state.
+//   * a plan lists scale, then live pages of block 0, then its special pages
+//     that hold a visible token, with last_page_len = 6*(f - fpp*(n_sp-1)),
+//     the runs of visible special tokens and the visible token count that
+//     these imply; check_run accepts exactly the blocks in that state;
+//   * the visible special tokens follow a model kept here: every frame shows
+//     its 6 specials until its page is evicted, then as many as the block's
+//     last eviction flags keep (6, the camera token only, or none).
 // tests/test_host_sanitizers.py builds it with g++ -fsanitize=address,
 // undefined (no GPU, no HIP) and runs it; any finding or broken invariant
 // ends the process with a non-zero status.
@@ -33,11 +37,11 @@ uint64_t g_state = 0;
 // How often each outcome was reached, so the caller can tell that every error
 // path of the allocator ran under the sanitizers.
 enum Outcome { kAppendOk, kExhausted, kOverflow, kUndo, kEvictMoved, kEvictDeferred,
-               kBadBlock, kUnsupported, kInvalid, kRollbackOk, kNothingToRollback,
+               kBadBlock, kSpecialsThinned, kInvalid, kRollbackOk, kNothingToRollback,
                kPlanOk, kPlanEmpty, kRunOk, kStale, kNotPlanned, kSmallCap, kNumOutcomes };
 const char* const kOutcomeName[kNumOutcomes] = {
     "append_ok", "pool_exhausted", "special_overflow", "undo_append", "evict_moved",
-    "evict_deferred", "bad_block", "unsupported", "invalid_arg", "rollback_ok",
+    "evict_deferred", "bad_block", "specials_thinned", "invalid_arg", "rollback_ok",
     "nothing_to_rollback", "plan_ok", "plan_empty", "run_ok", "stale_plan", "not_planned",
     "block_state_small_cap"};
 long g_count[kNumOutcomes] = {};
@@ -63,10 +67,32 @@ int rnd(int n) { return static_cast<int>(next_u64() % static_cast<uint64_t>(n));
 struct BlockSnap {
   std::vector<int32_t> scale, live, free_list;
   int64_t nsf = 0;
+  std::vector<spkv::SpecialRun> specials;
   bool operator==(const BlockSnap& o) const {
-    return scale == o.scale && live == o.live && free_list == o.free_list && nsf == o.nsf;
+    return scale == o.scale && live == o.live && free_list == o.free_list && nsf == o.nsf &&
+           specials == o.specials;
   }
 };
+
+// The driver's own model of which special tokens each block shows: per frame
+// of the special stream, how many of its specials are visible, and the count
+// the block's last eviction flags keep.
+struct Model {
+  std::vector<std::vector<int32_t>> vis;
+  std::vector<int32_t> kept;
+};
+
+// Runs of equal counts of a per-frame list, zero counts left out.
+std::vector<spkv::SpecialRun> runs_of(const std::vector<int32_t>& vis) {
+  std::vector<spkv::SpecialRun> out;
+  for (int32_t f = 0; f < static_cast<int32_t>(vis.size()); ++f) {
+    if (!out.empty() && out.back().kept == vis[f] && out.back().first + out.back().count == f)
+      ++out.back().count;
+    else if (vis[f] > 0)
+      out.push_back(spkv::SpecialRun{f, 1, vis[f]});
+  }
+  return out;
+}
 
 BlockSnap snap(const PagePool& p, int b) {
   const int32_t m = p.geometry().num_patch_pages;
@@ -80,6 +106,13 @@ BlockSnap snap(const PagePool& p, int b) {
   s.live.assign(lv.begin(), lv.begin() + nl);
   s.free_list.assign(fr.begin(), fr.begin() + nf);
   s.nsf = nsf;
+  int32_t n = -1;
+  REQUIRE(p.block_specials(b, nullptr, 0, &n) == Status::ok && n >= 0);
+  s.specials.resize(n);
+  if (n > 0) {
+    REQUIRE(p.block_specials(b, s.specials.data(), n - 1, &n) == Status::invalid_arg);
+    REQUIRE(p.block_specials(b, s.specials.data(), n, &n) == Status::ok);
+  }
   return s;
 }
 
@@ -89,9 +122,11 @@ std::vector<BlockSnap> snap_all(const PagePool& p) {
   return v;
 }
 
-void check_block(const PagePool& p, int b) {
+void check_block(const PagePool& p, const Model& md, int b) {
   const Geometry& g = p.geometry();
   const BlockSnap s = snap(p, b);
+  REQUIRE(static_cast<int64_t>(md.vis[b].size()) == s.nsf);
+  REQUIRE(s.specials == runs_of(md.vis[b]));
   std::vector<int> seen(g.num_patch_pages, 0);
   for (const auto* list : {&s.scale, &s.live, &s.free_list})
     for (int32_t x : *list) {
@@ -110,27 +145,38 @@ void check_block(const PagePool& p, int b) {
   REQUIRE(st.special_tokens == s.nsf * g.num_special);
 }
 
-void check_all(const PagePool& p) {
-  for (int b = 0; b < p.geometry().num_blocks; ++b) check_block(p, b);
+void check_all(const PagePool& p, const Model& md) {
+  for (int b = 0; b < p.geometry().num_blocks; ++b) check_block(p, md, b);
 }
 
-// The committed plan against block 0's state when it was built (`at`).
-void check_plan(const PagePool& p, const BlockSnap& at) {
+// The committed plan against block 0's state when it was built (`at`, and
+// the model's visible specials `vis` then).
+void check_plan(const PagePool& p, const BlockSnap& at, const std::vector<int32_t>& vis) {
   const Geometry& g = p.geometry();
   const spkv::PlanView v = p.plan_view();
   const int32_t fpp = g.frames_per_spage;
   const int32_t n_sp = static_cast<int32_t>((at.nsf + fpp - 1) / fpp);
   REQUIRE(v.n_patch == static_cast<int32_t>(at.scale.size() + at.live.size()));
-  REQUIRE(v.n_pages == v.n_patch + n_sp);
+  REQUIRE(v.n_pages <= v.n_patch + n_sp);
   REQUIRE(v.n_pages <= g.max_num_pages);
   int32_t i = 0;
   for (int32_t x : at.scale) REQUIRE(v.table[i++] == x);
   for (int32_t x : at.live) REQUIRE(v.table[i++] == x);
-  for (int32_t k = 0; k < n_sp; ++k) REQUIRE(v.table[i++] == g.num_patch_pages + k);
+  int64_t special_tokens = 0;
+  for (int32_t k = 0; k < n_sp; ++k) {
+    int32_t shown = 0;
+    for (int32_t f = k * fpp; f < std::min<int64_t>((k + 1) * fpp, at.nsf); ++f) shown += vis[f];
+    special_tokens += shown;
+    if (shown > 0) REQUIRE(v.table[i++] == g.num_patch_pages + k);
+  }
+  REQUIRE(i == v.n_pages);
+  REQUIRE(v.table[v.n_pages - 1] == g.num_patch_pages + n_sp - 1);
   REQUIRE(v.last_page_len == g.num_special * (at.nsf - int64_t(fpp) * (n_sp - 1)));
   REQUIRE(v.last_page_len >= g.num_special && v.last_page_len <= g.num_special * fpp);
-  REQUIRE(v.visible_tokens == int64_t(v.n_patch) * g.patch_tokens +
-                                  int64_t(n_sp - 1) * g.num_special * fpp + v.last_page_len);
+  REQUIRE(v.visible_tokens == int64_t(v.n_patch) * g.patch_tokens + special_tokens);
+  const std::vector<spkv::SpecialRun> want = runs_of(vis);
+  REQUIRE(v.n_segs == static_cast<int32_t>(want.size()));
+  REQUIRE(std::equal(want.begin(), want.end(), v.segs));
 }
 
 // Expects an error status and no state change.
@@ -142,10 +188,20 @@ void expect_error(const PagePool& p, const std::vector<BlockSnap>& before, Statu
 
 uint64_t run_sequence(const Geometry& g, int n_ops) {
   PagePool p(g);
-  check_all(p);
+  Model md;
+  md.vis.assign(g.num_blocks, {});
+  md.kept.assign(g.num_blocks, g.num_special);
+  check_all(p, md);
   const int32_t S = g.scale_frames, M = g.num_patch_pages;
   const int32_t wmax = M - S;
+  // The model's side of an eviction that moved `moved` pages of block b.
+  auto evicted = [&](int b, const BlockSnap& sb, int32_t moved) {
+    const int64_t oldest = sb.nsf - static_cast<int64_t>(sb.live.size());
+    for (int32_t i = 0; i < moved; ++i) md.vis[b][oldest + i] = md.kept[b];
+    if (moved > 0 && md.kept[b] < g.num_special) ++g_count[kSpecialsThinned];
+  };
   BlockSnap planned_at;
+  std::vector<int32_t> planned_vis;
   bool have_plan = false;
   uint64_t digest = 1469598103934665603ull;
   auto mix = [&](uint64_t x) { digest = (digest ^ x) * 1099511628211ull; };
@@ -173,39 +229,42 @@ uint64_t run_sequence(const Geometry& g, int n_ops) {
         REQUIRE(r.special_page < g.max_num_pages);
         REQUIRE(r.special_slot + g.num_special <= g.page_size);
         mix(uint64_t(r.patch_page) << 32 | uint32_t(r.special_slot));
+        md.vis[b].push_back(g.num_special);
         if (rnd(8) == 0) {
           p.undo_append(b, r);
+          md.vis[b].pop_back();
           REQUIRE(snap_all(p) == before);
           ++g_count[kUndo];
         }
       }
     } else if (kind < 48) {  // evict, mostly with valid arguments
       int32_t w = 1 + rnd(std::max(1, wmax));
-      int32_t s_arg = S, cfs = 1, cam = 0;
+      int32_t s_arg = S;
+      // the flags: mostly the defaults, else any valid pair
+      int32_t cfs = rnd(3) ? 1 : rnd(2), cam = rnd(3) ? 0 : rnd(2);
       int bb = b;
-      const int bad = rnd(10);
+      const int bad = rnd(12);
       if (bad == 0) s_arg = S + 1;
       if (bad == 1) w = rnd(2) ? 0 : wmax + 1;
-      if (bad == 2) cfs = 0;
-      if (bad == 3) cam = 1;
+      if (bad == 2) cfs = rnd(2) ? -1 : 2;
+      if (bad == 3) cam = rnd(2) ? -1 : 2;
       if (bad == 4) bb = rnd(2) ? -1 : g.num_blocks;
       int32_t moved = -1;
       const Status s = p.evict(bb, s_arg, w, cfs, cam, &moved);
       if (bad == 4) {
         expect_error(p, before, s, Status::bad_block);
         ++g_count[kBadBlock];
-      } else if (bad == 2 || bad == 3) {
-        expect_error(p, before, s, Status::unsupported);
-        ++g_count[kUnsupported];
-      } else if (bad <= 1) {
+      } else if (bad <= 3) {
         expect_error(p, before, s, Status::invalid_arg);
         ++g_count[kInvalid];
       } else {
         REQUIRE(s == Status::ok);
+        md.kept[b] = cfs ? (cam ? 1 : g.num_special) : 0;
         const int32_t live = static_cast<int32_t>(before[b].live.size());
         REQUIRE(moved == (p.defer() ? 0 : std::max(0, live - w)));
         if (p.defer() && live > w) ++g_count[kEvictDeferred];
         if (moved > 0) ++g_count[kEvictMoved];
+        evicted(b, before[b], moved);
         mix(uint64_t(moved));
       }
     } else if (kind < 56) {  // deferred eviction carried out
@@ -213,6 +272,7 @@ uint64_t run_sequence(const Geometry& g, int n_ops) {
       int32_t moved = -1;
       REQUIRE(p.execute_deferred(b, S, w, &moved) == Status::ok);
       REQUIRE(moved == std::max(0, static_cast<int32_t>(before[b].live.size()) - w));
+      evicted(b, before[b], moved);
     } else if (kind < 70) {  // rollback
       const Status s = p.rollback(b);
       if (s != Status::ok) {
@@ -220,6 +280,7 @@ uint64_t run_sequence(const Geometry& g, int n_ops) {
         ++g_count[kNothingToRollback];
       } else {
         ++g_count[kRollbackOk];
+        md.vis[b].pop_back();
         const BlockSnap after = snap(p, b);
         REQUIRE(after.nsf == before[b].nsf - 1);
         REQUIRE(after.free_list.size() == before[b].free_list.size() + 1);
@@ -229,6 +290,8 @@ uint64_t run_sequence(const Geometry& g, int n_ops) {
       p.set_defer(rnd(2) == 1);
     } else if (kind < 78) {
       p.reset();
+      md.vis.assign(g.num_blocks, {});
+      md.kept.assign(g.num_blocks, g.num_special);
       have_plan = false;
       for (int k = 0; k < g.num_blocks; ++k) {
         const BlockSnap s = snap(p, k);
@@ -247,8 +310,9 @@ uint64_t run_sequence(const Geometry& g, int n_ops) {
         ++g_count[kPlanOk];
         if (commit) {
           planned_at = before[0];
+          planned_vis = md.vis[0];
           have_plan = true;
-          check_plan(p, planned_at);
+          check_plan(p, planned_at, planned_vis);
           mix(uint64_t(p.plan_view().visible_tokens));
         }
       }
@@ -260,7 +324,7 @@ uint64_t run_sequence(const Geometry& g, int n_ops) {
       } else {
         const BlockSnap sb = before[b];
         const bool same = sb.nsf == planned_at.nsf && sb.scale == planned_at.scale &&
-                          sb.live == planned_at.live;
+                          sb.live == planned_at.live && md.vis[b] == planned_vis;
         REQUIRE(s == (same ? Status::ok : Status::stale_plan));
         ++g_count[same ? kRunOk : kStale];
       }
@@ -278,7 +342,7 @@ uint64_t run_sequence(const Geometry& g, int n_ops) {
       REQUIRE(s == (fits ? Status::ok : Status::invalid_arg));
       if (!fits) ++g_count[kSmallCap];
     }
-    check_all(p);
+    check_all(p, md);
   }
   return digest;
 }

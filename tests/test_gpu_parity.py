@@ -14,6 +14,7 @@ import synth
 import harness as H
 from oracle import OracleConfig, PagePoolOracle
 from oracle.attention import paged_attention
+from oracle.pagepool import special_runs
 
 pytestmark = pytest.mark.gpu
 
@@ -35,9 +36,10 @@ def log(msg):
 
 
 # ------------------------------------------------------------ small streams
-def full_parity(wl, frames=None, splits=0):
-    """Every frame: whole-pool bytes, plan, stats, state bit-exact; attention
-    on every row of every block."""
+def full_parity(wl, frames=None, splits=0, flags=(1, 0)):
+    """Every frame: whole-pool bytes, plan (with its visible special runs),
+    stats, state bit-exact; attention on every row of every block.  Every
+    evict_frames call passes the eviction flags."""
     need_gpu()
     cache = new_cache(wl)
     if splits:
@@ -60,13 +62,14 @@ def full_parity(wl, frames=None, splits=0):
             o.set_defer_eviction(True)
         for b in range(wl.num_blocks):
             o.append_frame(b, bits[b][1], bits[b][2])
-            o.evict_frames(b, S, W)
+            o.evict_frames(b, S, W, *flags)
             if b == 0:
                 o.plan()
             pl = o.check_run(b)
             ref[b] = paged_attention(o.pools[b], pl, cfg, bits[b][0], sm)
         plan_ref = (list(o.plan_state.table), o.plan_state.n_patch,
                     o.plan_state.last_page_len)
+        specials_ref = special_runs(o.plan_state.spec_vis)
         for b in range(wl.num_blocks):
             if kind in ("transient", "reject"):
                 o.rollback_last_frame(b)
@@ -75,10 +78,12 @@ def full_parity(wl, frames=None, splits=0):
         if kind == "transient":
             o.set_defer_eviction(False)
 
-        H.gpu_step(cache, wl, kind, reset, qkv, outs)
+        H.gpu_step(cache, wl, kind, reset, qkv, outs, flags=flags)
         torch.cuda.synchronize()
         assert cache.get_plan() == plan_ref, f
+        assert cache.get_plan_specials() == specials_ref, f
         for b in range(wl.num_blocks):
+            assert o.special_visibility(b) == cache.get_block_specials(b), (f, b)
             assert list(o.block_state(b)) == list(cache.get_block_state(b)), (f, b)
             assert tuple(o.get_cache_stats(b)) == cache.get_cache_stats(b), (f, b)
             assert np.array_equal(synth.bf16_bits(cache.pools[b]), o.pools[b]), (f, b)
@@ -104,6 +109,28 @@ def test_tiny_stream_interval_reset_and_rollback():
 
 MID = synth.Workload("mid-ragged", 2, 16, 64, 203, 200, 6, 2, 6, 2, 64, 16,
                      keyframe_interval=2, seed=21)
+
+
+@pytest.mark.parametrize("flags", [(1, 1), (0, 0)])
+def test_tiny_stream_eviction_flags(flags):
+    """Evicted frames keep only their camera token, or none of their specials:
+    the row map skips the hidden special slots (and the special pages left
+    with none), the pool bytes do not change.  Keyframes, interval 2 with a
+    reset, and accept/rollback under deferral (the deferred flags apply)."""
+    tiny = synth.WORKLOADS["tiny"]
+    log(f"tiny stream, flags {flags}")
+    full_parity(tiny, flags=flags)
+    full_parity(tiny.with_(keyframe_interval=2, frames=14, reset_every=9), flags=flags)
+    full_parity(tiny.with_(dynamic=True, frames=20, seed=12), flags=flags)
+
+
+@pytest.mark.parametrize("flags,splits", [((1, 1), 0), ((0, 0), 3), ((0, 1), 7)])
+def test_mid_stream_eviction_flags(flags, splits):
+    """200-token patch pages (33 frames per special page) with the special
+    stream thinned to camera tokens or cut to the held frames, key-range
+    splits crossing the special runs."""
+    log(f"mid stream, flags {flags}, splits {splits}")
+    full_parity(MID.with_(frames=60), flags=flags, splits=splits)
 
 
 @pytest.mark.parametrize("splits", [0, 1, 3, 7])
@@ -473,7 +500,7 @@ def test_constant_v_is_reproduced():
 
 # ------------------------------------------------------- full-size streams
 def full_size(name, num_blocks=None, attn_blocks=(0, 11, 23), pool_blocks=(0, 23),
-              frames=None, milestone_keys=None):
+              frames=None, milestone_keys=None, flags=(1, 0)):
     """The workload's whole stream on the GPU, with the oracle checking every
     plan and state bit-exact, and at milestone frames the attention of
     sampled rows (all heads) and the bytes of the visible pages."""
@@ -484,7 +511,7 @@ def full_size(name, num_blocks=None, attn_blocks=(0, 11, 23), pool_blocks=(0, 23
     nb = wl.num_blocks
     attn_blocks = [b for b in attn_blocks if b < nb]
     pool_blocks = [b for b in pool_blocks if b < nb]
-    kinds, plans, writers_at, ms = H.dry_run(wl, frames)
+    kinds, plans, writers_at, ms = H.dry_run(wl, frames, flags=flags)
     milestones = sorted(set(ms.values()))
     need = H.needed_frames(wl, plans, writers_at, milestones)
     log(f"{name}: {len(kinds)} frames, {nb} blocks, milestones {ms}")
@@ -525,7 +552,7 @@ def full_size(name, num_blocks=None, attn_blocks=(0, 11, 23), pool_blocks=(0, 23
         for b in range(nb):
             k, v = kv_of(b)
             o.append_frame(b, k, v)
-            o.evict_frames(b, S, W)
+            o.evict_frames(b, S, W, *flags)
             if b == 0:
                 o.plan()
             pl = o.check_run(b)
@@ -546,9 +573,11 @@ def full_size(name, num_blocks=None, attn_blocks=(0, 11, 23), pool_blocks=(0, 23
         if kind == "transient":
             o.set_defer_eviction(False)
 
+        specials_ref = special_runs(o.plan_state.spec_vis)
         # HIP side
-        H.gpu_step(cache, wl, kind, reset, qkv, outs)
+        H.gpu_step(cache, wl, kind, reset, qkv, outs, flags=flags)
         assert cache.get_plan() == plan_ref, f
+        assert cache.get_plan_specials() == specials_ref, f
         if f in milestones:
             torch.cuda.synchronize()
             for b in range(nb):
@@ -576,17 +605,30 @@ def test_full_518x378_exact_stream():
 
 
 def test_full_518x378_padded_long_stream():
-    # 4096 frames; three blocks (the kernel's launch shape depends on the
-    # query count, heads and visible tokens, not on the number of blocks)
-    full_size("518x378-padded", num_blocks=3, attn_blocks=(0, 2), pool_blocks=(0, 2))
+    # 4096 frames (2048 keyframes) on all 24 blocks
+    full_size("518x378-padded")
 
 
 def test_full_dynamic_stream():
     full_size("dynamic")
 
 
+def test_full_518x378_stream_camera_tokens_only():
+    """The 518x378 stream with camera_only: from the first eviction on, each
+    evicted frame leaves its camera token in view; four blocks."""
+    full_size("518x378", num_blocks=4, attn_blocks=(0, 3), pool_blocks=(0, 3),
+              flags=(1, 1))
+
+
+def test_full_dynamic_stream_without_cross_frame_specials():
+    """The dynamic stream with cross_frame_special = 0: accepted frames'
+    deferred evictions drop the evicted frames' specials; four blocks."""
+    full_size("dynamic", num_blocks=4, attn_blocks=(0, 3), pool_blocks=(0, 3),
+              flags=(0, 0))
+
+
 # ------------------------------------------------- run_own (skip append)
-def own_parity(wl, check_frames=None, rows=None, splits=0):
+def own_parity(wl, check_frames=None, rows=None, splits=0, flags=(1, 0)):
     """A stream where keyframes are appended and every non-keyframe attends
     through run_own over the committed cache plus its own K/V, with no
     append.  Checked at the chosen non-keyframes: attention against the
@@ -606,11 +648,11 @@ def own_parity(wl, check_frames=None, rows=None, splits=0):
         q, k, v = synth.frame_qkv(wl, f, 0, device=DEV)
         if synth.is_keyframe(wl, f):
             cache.append_frame(0, k, v)
-            cache.evict_frames(0, S, W)
+            cache.evict_frames(0, S, W, *flags)
             cache.plan()
             cache.run(0, q)
             o.append_frame(0, synth.bf16_bits(k), synth.bf16_bits(v))
-            o.evict_frames(0, S, W)
+            o.evict_frames(0, S, W, *flags)
             o.plan()
             continue
         if check_frames is not None and f not in check_frames:
@@ -632,6 +674,14 @@ def own_parity(wl, check_frames=None, rows=None, splits=0):
             f"{wl.tokens_per_frame} own tokens")
     cache.close()
     assert checked > 0
+
+
+@pytest.mark.parametrize("flags", [(1, 1), (0, 0)])
+def test_run_own_with_eviction_flags(flags):
+    """run_own's row map (plan tokens, then the caller's own rows) when the
+    plan's special runs skip evicted frames' specials."""
+    log(f"run_own, mid stream, flags {flags}")
+    own_parity(MID.with_(num_blocks=1, frames=40), splits=3, flags=flags)
 
 
 @pytest.mark.parametrize("splits", [0, 1, 5])

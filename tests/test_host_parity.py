@@ -7,6 +7,7 @@ from hypothesis import given, settings, strategies as st
 
 import streaming_paged_kv_amd as spkv
 from oracle import OracleConfig, OracleError, PagePoolOracle
+from oracle.pagepool import special_runs
 import synth
 
 
@@ -31,11 +32,14 @@ def assert_same(o, c):
     for b in range(cfg.num_blocks):
         assert list(o.block_state(b)) == list(c.get_block_state(b)), b
         assert tuple(o.get_cache_stats(b)) == c.get_cache_stats(b), b
+        assert o.special_visibility(b) == c.get_block_specials(b), b
     if o.plan_state is None:
         assert code_of(c.get_plan) == "NOT_PLANNED"
+        assert code_of(c.get_plan_specials) == "NOT_PLANNED"
     else:
         pl = o.plan_state
         assert c.get_plan() == (pl.table, pl.n_patch, pl.last_page_len)
+        assert c.get_plan_specials() == special_runs(pl.spec_vis)
 
 
 def step(o, c, op, block, arg):
@@ -50,8 +54,11 @@ def step(o, c, op, block, arg):
         r = (code_of(o.evict_frames, block, cfg.scale_frames + 1, cfg.sliding_window),
              code_of(c.evict_frames, block, cfg.scale_frames + 1, cfg.sliding_window))
     elif op == "evict_flags":
-        r = (code_of(o.evict_frames, block, cfg.scale_frames, cfg.sliding_window, 0, 1),
-             code_of(c.evict_frames, block, cfg.scale_frames, cfg.sliding_window, 0, 1))
+        # arg picks the flags: every valid pair and two invalid ones
+        cfs, cam = [(0, 0), (0, 1), (1, 1), (1, 0), (2, 0), (1, -1), (0, 0)][arg]
+        w = 1 + (arg + block) % (cfg.num_patch_pages - cfg.scale_frames)
+        r = (code_of(o.evict_frames, block, cfg.scale_frames, w, cfs, cam),
+             code_of(c.evict_frames, block, cfg.scale_frames, w, cfs, cam))
     elif op == "defer":
         r = (code_of(o.set_defer_eviction, bool(arg)),
              code_of(c.set_defer_eviction, bool(arg)))
@@ -90,7 +97,7 @@ CFGS = [
 op_strategy = st.tuples(
     st.sampled_from(["append", "append", "append", "evict", "evict", "defer",
                      "execute", "rollback", "plan", "plan", "run", "run_own", "reset",
-                     "evict_badS", "evict_flags"]),
+                     "evict_badS", "evict_flags", "evict_flags"]),
     st.integers(-1, 3), st.integers(0, 6))
 
 
@@ -123,10 +130,50 @@ def test_tiny_stream_worked_example_through_abi(golden_dir):
     c.close()
 
 
-@pytest.mark.parametrize("name", ["224x224", "518x378", "518x378-padded", "dynamic"])
-def test_full_stream_schedules_match_oracle(name):
+def test_eviction_flags_worked_example_through_abi(golden_dir):
+    """The hand-derived eviction-flag example, replayed on the C++ allocator."""
+    import json, os
+    g = json.load(open(os.path.join(golden_dir, "eviction_flags_tiny.json")))
+    cfg = g["config"]
+    S, W = cfg["scale_frames"], cfg["sliding_window"]
+    for sc in g["scenarios"]:
+        c = spkv.PagedKVCache(host_only=True, **cfg)
+        checks = {row["t"]: row for row in sc["checks"]}
+        flags, n = sc["flags"]
+        sched = [tuple(flags)] * n + [tuple(x) for x in sc.get("then", [])]
+        for t, fl in enumerate(sched):
+            c.append_frame(0)
+            c.evict_frames(0, S, W, *fl)
+            c.plan()
+            if t in checks:
+                row = checks[t]
+                assert c.get_plan()[0] == row["table"], (sc["name"], t)
+                assert c.get_plan()[2] == row["last_page_len"]
+                assert c.get_plan_specials() == row["specials"], (sc["name"], t)
+                assert c.get_block_specials(0) == row["specials"]
+        d = sc.get("deferred")
+        if d:
+            c.set_defer_eviction(True)
+            c.append_frame(0)
+            c.evict_frames(0, S, W, 0, 0)
+            c.execute_deferred_eviction(0, S, W)
+            c.set_defer_eviction(False)
+            c.plan()
+            assert c.get_plan()[0] == d["table"]
+            assert c.get_plan()[2] == d["last_page_len"]
+            assert c.get_plan_specials() == d["specials"]
+            assert c.get_block_state(0)[2] == d["free"]
+        c.close()
+
+
+@pytest.mark.parametrize("name,flags", [
+    ("224x224", (1, 0)), ("518x378", (1, 0)), ("518x378-padded", (1, 0)), ("dynamic", (1, 0)),
+    ("518x378", (1, 1)), ("dynamic", (0, 0)), ("224x224", (0, 1))])
+def test_full_stream_schedules_match_oracle(name, flags):
     """The whole frame schedule of each workload (all blocks, every frame),
-    bit-exact on every block's state and on every plan."""
+    bit-exact on every block's state and on every plan, with the pages'
+    default eviction flags and with the variants that thin or drop the
+    specials of evicted frames."""
     wl = synth.WORKLOADS[name]
     cfg = wl.cfg_kwargs()
     o, c = make_pair(**cfg)
@@ -148,11 +195,12 @@ def test_full_stream_schedules_match_oracle(name):
             o.set_defer_eviction(True); c.set_defer_eviction(True)
         for b in range(nb):
             o.append_frame(b); c.append_frame(b)
-            o.evict_frames(b, S, W); c.evict_frames(b, S, W)
+            o.evict_frames(b, S, W, *flags); c.evict_frames(b, S, W, *flags)
             if b == 0:
                 o.plan(); c.plan()
                 pl = o.plan_state
                 assert c.get_plan() == (pl.table, pl.n_patch, pl.last_page_len), f
+                assert c.get_plan_specials() == special_runs(pl.spec_vis), f
             o.check_run(b)
             assert code_of(c.run, b) == "UNSUPPORTED"
         for b in range(nb):
