@@ -46,6 +46,10 @@ def parse():
                          "and the live window")
     ap.add_argument("--workload", default="518x378")
     ap.add_argument("--bank", type=int, default=16, help="distinct input frames")
+    ap.add_argument("--append", choices=("in_run", "plain"), default="in_run",
+                    help="in_run: keyframes are admitted with append_frame_in_run, so "
+                         "each block's run copies the frame inside the attention "
+                         "launch; plain: append_frame launches its own copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2,
                     help="blocks of the oracle frame timed (scaled to all)")
@@ -428,6 +432,8 @@ def main():
                 (nsp - 1) * wl.num_special_tokens *
                 (wl.page_size // wl.num_special_tokens) + lpl)
 
+    admit = cache.append_frame_in_run if args.append == "in_run" else cache.append_frame
+
     def step(f, mode):
         kind = sched[f]
         qkv = bank[f % nbank]
@@ -472,7 +478,7 @@ def main():
         for b in range(nb):
             q, k, v = qkv[b]
             if mode != "C":
-                cache.append_frame(b, k, v, stream=stream)
+                admit(b, k, v, stream=stream)
             cache.evict_frames(b, S, W)
             if b == 0:
                 cache.plan(stream=stream)
@@ -558,6 +564,10 @@ def main():
                                f"{W}-page live window, then --warmup {args.warmup}"),
             "visible_tokens_timed": [nk_lo, nk_hi],
             "input_bank_frames": nbank,
+            "keyframe_append": ("append_frame_in_run: each block's run copies the frame "
+                                "into its pages inside the attention launch"
+                                if args.append == "in_run" else
+                                "append_frame: one copy launch per block"),
         },
     }
     if full is not None:
@@ -590,8 +600,8 @@ def main():
             "unit": "GB/s", "frac": app_gbs / PEAK_HBM_GBS,
             "avg_launch_us": sum(t_app) / n_launch * 1e6,
             "window": (f"keyframes among frames {total}..{total + n_app - 1}: per frame, "
-                       f"events around its {nb} appends issued back to back (launch "
-                       f"gaps included)"),
+                       f"events around its {nb} plain appends (append_frame) issued back "
+                       f"to back (launch gaps included)"),
             "bytes_per_launch": app_bytes[0] // nb,
         }
     cache.close()

@@ -149,6 +149,22 @@ SPKV_API int spkv_destroy(spkv_handle* h);
 SPKV_API int spkv_append_frame(spkv_handle* h, int32_t block, const void* k,
                                const void* v, void* hip_stream);
 
+/* append_frame with its copy folded into the block's next run() ([LB-KV]
+ * "Append and Evict API" for the admission; the pages' streaming loop
+ * appends, evicts, plans on block 0 and runs each block in turn, "Streaming
+ * Forward Pass").  Admits the frame exactly like spkv_append_frame (same
+ * state change, same errors) but enqueues nothing: the next spkv_run of this
+ * block copies the frame into its pages inside the attention launch and
+ * reads the frame's own tokens from k and v, so a keyframe costs no separate
+ * copy launch.  If another call needs the bytes first -- the block's next
+ * append, its rollback, run_own, run_noalloc, a run_batch holding the block,
+ * a run that cannot fold the copy (a pool over 2 GiB, or a plan that is not
+ * the one of this frame), reset or destroy -- the library enqueues the plain
+ * copy on hip_stream first.  k and v must therefore stay valid and unchanged
+ * until that copy has run (the pool's bytes end up the same either way). */
+SPKV_API int spkv_append_frame_in_run(spkv_handle* h, int32_t block, const void* k,
+                                      const void* v, void* hip_stream);
+
 /* evict_frames(block_idx, scale_frames, sliding_window, cross_frame_special,
  * camera_only) ([LB-KV] "Append and Evict API", "Streaming Forward Pass").
  * While the live window holds more than sliding_window pages, its oldest page

@@ -50,6 +50,7 @@ ERROR_NAMES = {
 # Symbols the header declares (checked by the CPU tests).
 EXPORTED = (
     "spkv_query_sizes", "spkv_query_workspace", "spkv_create", "spkv_destroy", "spkv_append_frame",
+    "spkv_append_frame_in_run",
     "spkv_evict_frames", "spkv_set_defer_eviction",
     "spkv_execute_deferred_eviction", "spkv_rollback_last_frame", "spkv_reset",
     "spkv_plan", "spkv_run", "spkv_run_noalloc", "spkv_run_own", "spkv_run_batch", "spkv_set_num_splits",
@@ -112,6 +113,7 @@ def load_library(path=None):
                         ctypes.POINTER(vp)],
         "spkv_destroy": [vp],
         "spkv_append_frame": [vp, i32, vp, vp, vp],
+        "spkv_append_frame_in_run": [vp, i32, vp, vp, vp],
         "spkv_evict_frames": [vp, i32, i32, i32, i32, i32],
         "spkv_set_defer_eviction": [vp, i32],
         "spkv_execute_deferred_eviction": [vp, i32, i32, i32],
@@ -231,6 +233,7 @@ class PagedKVCache:
                 _check(self.lib.spkv_create(ctypes.byref(self._c), ptrs,
                                             ctypes.c_void_p(self.workspace.data_ptr()),
                                             ws, ctypes.byref(self._h)), "spkv_create")
+        self._held = {}   # frames whose copy append_frame_in_run left to a later call
         dbg = os.environ.get("SPKV_DEBUG_KV", "")
         self._debug_every = int(dbg) if dbg.isdigit() and int(dbg) > 0 else 0
         self._plans = 0
@@ -272,6 +275,22 @@ class PagedKVCache:
         vp = self._frame_tensor(v, "v", self.tokens_per_frame)
         _check(self.lib.spkv_append_frame(self._h, block, kp, vp, _stream_ptr(stream)),
                "spkv_append_frame")
+
+    def append_frame_in_run(self, block, k=None, v=None, stream=None):
+        """append_frame whose copy into the pool is done by this block's next
+        run() (inside the attention launch), or earlier by a plain copy when
+        another call needs the bytes first.  k and v are kept referenced here
+        until the block's next append, so they stay valid for that copy."""
+        if self.host_only:
+            _check(self.lib.spkv_append_frame_in_run(self._h, block, None, None, None),
+                   "spkv_append_frame_in_run")
+            return
+        kp = self._frame_tensor(k, "k", self.tokens_per_frame)
+        vp = self._frame_tensor(v, "v", self.tokens_per_frame)
+        _check(self.lib.spkv_append_frame_in_run(self._h, block, kp, vp,
+                                                 _stream_ptr(stream)),
+               "spkv_append_frame_in_run")
+        self._held[block] = (k, v)
 
     def evict_frames(self, block, scale_frames, sliding_window,
                      cross_frame_special=1, camera_only=0):

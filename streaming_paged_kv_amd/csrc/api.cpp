@@ -83,7 +83,9 @@ Sizes sizes_of(const spkv::Geometry& g) {
   s.rowmap_own_bytes =
       round_up((round_up(int64_t(g.max_num_pages) * g.page_size + g.tokens_per_frame,
                          spkv::kAttnKeyTile) + spkv::kRowmapPad) * 4, kAlign);
-  s.min_ws = 2 * s.table_bytes + 2 * s.rowmap_bytes + 2 * s.rowmap_own_bytes;
+  // run()'s map, run_own()'s map and the map of a run that copies the newest
+  // frame (append_frame_in_run), each double-buffered.
+  s.min_ws = 2 * s.table_bytes + 4 * s.rowmap_bytes + 2 * s.rowmap_own_bytes;
   return s;
 }
 
@@ -123,6 +125,16 @@ struct spkv_handle {
   int32_t* dev_table[2] = {nullptr, nullptr};
   uint32_t* dev_rowmap[2] = {nullptr, nullptr};
   uint32_t* dev_rowmap_own[2] = {nullptr, nullptr};
+  uint32_t* dev_rowmap_new[2] = {nullptr, nullptr};
+  // A frame admitted by append_frame_in_run whose copy into the pool has not
+  // been enqueued yet (at most one per block: it is the block's newest frame).
+  struct Pending {
+    bool set = false;
+    spkv::AppendArgs copy{};
+    int32_t patch_page = -1;
+    hipStream_t stream = nullptr;
+  };
+  std::vector<Pending> pending;
   char* stage = nullptr;             // pinned, 2 x table_bytes
   hipEvent_t copied[2] = {nullptr, nullptr};
   bool copy_pending[2] = {false, false};
@@ -133,6 +145,48 @@ struct spkv_handle {
   int forced_splits = 0;
   int num_cus = 256;
 };
+
+namespace {
+
+// The copy of an admitted frame into its pages.
+spkv::AppendArgs append_args(const spkv_handle* h, int32_t block, const void* k,
+                             const void* v, const spkv::AppendResult& r) {
+  const spkv::Geometry& g = h->g;
+  const int64_t hd = int64_t(g.num_heads) * g.head_dim;
+  const int64_t page = int64_t(g.page_size) * hd;
+  spkv::AppendArgs a;
+  a.k = k;
+  a.v = v;
+  a.pool = h->pools[block];
+  a.patch_k_off = (int64_t(r.patch_page) * 2 + 0) * page;
+  a.patch_v_off = (int64_t(r.patch_page) * 2 + 1) * page;
+  a.special_k_off = (int64_t(r.special_page) * 2 + 0) * page + int64_t(r.special_slot) * hd;
+  a.special_v_off = (int64_t(r.special_page) * 2 + 1) * page + int64_t(r.special_slot) * hd;
+  a.patch_elems = int64_t(g.patch_tokens) * hd;
+  a.special_elems = int64_t(g.num_special) * hd;
+  return a;
+}
+
+// Enqueues block's pending copy (append_frame_in_run), if any, on the stream
+// that call named.
+int flush_pending(spkv_handle* h, int32_t block) {
+  spkv_handle::Pending& p = h->pending[block];
+  if (!p.set) return SPKV_OK;
+  DeviceGuard guard(h->device);
+  if (spkv::launch_append(p.copy, p.stream) != hipSuccess) return SPKV_ERR_HIP;
+  p.set = false;
+  return SPKV_OK;
+}
+
+int flush_all(spkv_handle* h) {
+  for (int32_t b = 0; b < static_cast<int32_t>(h->pending.size()); ++b) {
+    const int rc = flush_pending(h, b);
+    if (rc != SPKV_OK) return rc;
+  }
+  return SPKV_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -228,6 +282,10 @@ SPKV_API int spkv_create(const spkv_config* cfg, void* const* pool_ptrs,
                                                      2 * sz.rowmap_bytes);
   h->dev_rowmap_own[1] = reinterpret_cast<uint32_t*>(
       h->ws + 2 * sz.table_bytes + 2 * sz.rowmap_bytes + sz.rowmap_own_bytes);
+  for (int i = 0; i < 2; ++i)
+    h->dev_rowmap_new[i] = reinterpret_cast<uint32_t*>(
+        h->ws + 2 * sz.table_bytes + (2 + i) * sz.rowmap_bytes + 2 * sz.rowmap_own_bytes);
+  h->pending.assign(g.num_blocks, spkv_handle::Pending{});
   h->partials = h->ws + sz.min_ws;
   // The device address of run_noalloc()'s scratch, looked up once per device
   // with that device current.
@@ -256,6 +314,7 @@ SPKV_API int spkv_destroy(spkv_handle* h) {
   int rc = SPKV_OK;
   if (!h->host_only) {
     DeviceGuard guard(h->device);
+    rc = flush_all(h);
     for (int i = 0; i < 2; ++i) {
       if (h->copy_pending[i] && hipEventSynchronize(h->copied[i]) != hipSuccess)
         rc = SPKV_ERR_HIP;
@@ -275,6 +334,8 @@ SPKV_API int spkv_append_frame(spkv_handle* h, int32_t block, const void* k,
     if (k || v) return SPKV_ERR_INVALID_ARG;
   } else {
     if (!k || !v || !aligned16(k) || !aligned16(v)) return SPKV_ERR_INVALID_ARG;
+    const int f = flush_pending(h, block);
+    if (f != SPKV_OK) return f;
   }
   spkv::AppendResult r;
   const spkv::Status s = h->pool->append(block, &r);
@@ -282,23 +343,34 @@ SPKV_API int spkv_append_frame(spkv_handle* h, int32_t block, const void* k,
   if (h->host_only) return SPKV_OK;
 
   DeviceGuard guard(h->device);
-  const spkv::Geometry& g = h->g;
-  const int64_t hd = int64_t(g.num_heads) * g.head_dim;
-  const int64_t page = int64_t(g.page_size) * hd;
-  spkv::AppendArgs a;
-  a.k = k;
-  a.v = v;
-  a.pool = h->pools[block];
-  a.patch_k_off = (int64_t(r.patch_page) * 2 + 0) * page;
-  a.patch_v_off = (int64_t(r.patch_page) * 2 + 1) * page;
-  a.special_k_off = (int64_t(r.special_page) * 2 + 0) * page + int64_t(r.special_slot) * hd;
-  a.special_v_off = (int64_t(r.special_page) * 2 + 1) * page + int64_t(r.special_slot) * hd;
-  a.patch_elems = int64_t(g.patch_tokens) * hd;
-  a.special_elems = int64_t(g.num_special) * hd;
-  if (spkv::launch_append(a, static_cast<hipStream_t>(hip_stream)) != hipSuccess) {
+  if (spkv::launch_append(append_args(h, block, k, v, r),
+                          static_cast<hipStream_t>(hip_stream)) != hipSuccess) {
     h->pool->undo_append(block, r);
     return SPKV_ERR_HIP;
   }
+  return SPKV_OK;
+}
+
+SPKV_API int spkv_append_frame_in_run(spkv_handle* h, int32_t block, const void* k,
+                                      const void* v, void* hip_stream) {
+  if (!h) return SPKV_ERR_INVALID_ARG;
+  if (block < 0 || block >= h->g.num_blocks) return SPKV_ERR_BAD_BLOCK;
+  if (h->host_only) {
+    if (k || v) return SPKV_ERR_INVALID_ARG;
+  } else {
+    if (!k || !v || !aligned16(k) || !aligned16(v)) return SPKV_ERR_INVALID_ARG;
+    const int f = flush_pending(h, block);
+    if (f != SPKV_OK) return f;
+  }
+  spkv::AppendResult r;
+  const spkv::Status s = h->pool->append(block, &r);
+  if (s != spkv::Status::ok) return status(s);
+  if (h->host_only) return SPKV_OK;
+  spkv_handle::Pending& p = h->pending[block];
+  p.copy = append_args(h, block, k, v, r);
+  p.patch_page = r.patch_page;
+  p.stream = static_cast<hipStream_t>(hip_stream);
+  p.set = true;
   return SPKV_OK;
 }
 
@@ -327,11 +399,20 @@ SPKV_API int spkv_execute_deferred_eviction(spkv_handle* h, int32_t block,
 
 SPKV_API int spkv_rollback_last_frame(spkv_handle* h, int32_t block) {
   if (!h) return SPKV_ERR_INVALID_ARG;
+  // the frame's bytes are written whether it stays or not
+  if (!h->host_only && block >= 0 && block < h->g.num_blocks) {
+    const int f = flush_pending(h, block);
+    if (f != SPKV_OK) return f;
+  }
   return status(h->pool->rollback(block));
 }
 
 SPKV_API int spkv_reset(spkv_handle* h) {
   if (!h) return SPKV_ERR_INVALID_ARG;
+  if (!h->host_only) {
+    const int f = flush_all(h);
+    if (f != SPKV_OK) return f;
+  }
   h->pool->reset();
   return SPKV_OK;
 }
@@ -379,6 +460,8 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream) {
   pa.n_out = static_cast<int32_t>(
       round_up(pv.visible_tokens, spkv::kAttnKeyTile) + spkv::kRowmapPad);
   pa.rowmap_own = h->dev_rowmap_own[slot];
+  pa.rowmap_new = h->dev_rowmap_new[slot];
+  pa.new_patch_begin = (pv.n_patch - 1) * g.patch_tokens;
   pa.n_own = g.tokens_per_frame;
   pa.n_out_own = static_cast<int32_t>(
       round_up(pv.visible_tokens + g.tokens_per_frame, spkv::kAttnKeyTile) +
@@ -486,6 +569,7 @@ spkv::AttnArgs make_run(spkv_handle* h, int32_t block, const void* q, void* out,
 
   const bool own = own_k != nullptr;
   spkv::AttnArgs a;
+  a.copy = spkv::FrameCopy{};
   a.pool = static_cast<const uint16_t*>(h->pools[block]);
   a.own_k = static_cast<const uint16_t*>(own_k);
   a.own_v = static_cast<const uint16_t*>(own_v);
@@ -521,16 +605,41 @@ int run_impl(spkv_handle* h, int32_t block, const void* q, void* out, int32_t nq
   const int rc = check_run(h, block, q, out, nq, sm_scale, own_k, own_v, &shape);
   if (rc != SPKV_OK) return rc;
   if (noalloc && nq > noalloc_max_rows(h->g)) return SPKV_ERR_WORKSPACE;
+  // A frame admitted by append_frame_in_run is copied by this launch when the
+  // run reads the plan's pages alone and the plan's newest frame is it; its
+  // rows are then read from the caller's buffers (the own-row mark needs a
+  // pool of at most 2 GiB).  Otherwise its copy is enqueued first.
+  const spkv::PlanView pv = h->pool->plan_view();
+  spkv_handle::Pending& pend = h->pending[block];
+  const bool fuse = pend.set && !own_k && !noalloc &&
+                    h->sz.pool_bytes <= (int64_t(1) << 31) &&
+                    pv.table[pv.n_patch - 1] == pend.patch_page;
+  if (pend.set && !fuse) {
+    const int f = flush_pending(h, block);
+    if (f != SPKV_OK) return f;
+  }
   // One resident workgroup per CU; each split keeps >= 4 key tiles.
   int64_t want = (int64_t(h->num_cus) + shape.units - 1) / shape.units;
   want = std::min<int64_t>(want, std::max<int64_t>(1, shape.n_ktiles / 4));
   const Partials part = noalloc ? Partials{h->scratch, spkv::kScratchBytes}
                                 : workspace_partials(h);
-  const spkv::AttnArgs a =
+  spkv::AttnArgs a =
       make_run(h, block, q, out, nq, sm_scale, own_k, own_v, shape, want, part);
+  if (fuse) {
+    const spkv::AppendArgs& c = pend.copy;
+    a.own_k = static_cast<const uint16_t*>(c.k);
+    a.own_v = static_cast<const uint16_t*>(c.v);
+    a.rowmap = h->dev_rowmap_new[h->plan_slot];
+    a.n_cached = (pv.n_patch - 1) * h->g.patch_tokens;  // first row read from k, v
+    a.copy = spkv::FrameCopy{a.own_k, a.own_v, static_cast<uint16_t*>(c.pool),
+                             c.patch_k_off / 8, c.patch_v_off / 8, c.special_k_off / 8,
+                             c.special_v_off / 8, static_cast<int32_t>(c.patch_elems / 8),
+                             static_cast<int32_t>(c.special_elems / 8)};
+  }
   DeviceGuard guard(h->device);
   if (spkv::launch_attention(a, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
     return SPKV_ERR_HIP;
+  if (fuse) pend.set = false;
   return SPKV_OK;
 }
 
@@ -608,6 +717,11 @@ SPKV_API int spkv_run_batch(const spkv_request* reqs, int32_t n, void* hip_strea
     if (rc != SPKV_OK && !(host_only && rc == SPKV_ERR_UNSUPPORTED)) return rc;
   }
   if (host_only) return SPKV_ERR_UNSUPPORTED;
+  // Frames admitted by append_frame_in_run are copied before the batch.
+  for (int32_t i = 0; i < n; ++i) {
+    const int f = flush_pending(reqs[i].handle, reqs[i].block);
+    if (f != SPKV_OK) return f;
+  }
   // Batch plan: split each request's key range so that every work item
   // (query tile x head x split) covers at most per_item key tiles, with the
   // smallest per_item (>= 4) whose items still fit the CUs once.

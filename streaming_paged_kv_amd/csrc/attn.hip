@@ -110,7 +110,20 @@ __device__ __forceinline__ uint32_t plan_row(const PlanArgs& p, int t) {
 
 __global__ __launch_bounds__(256) void expand_kernel(PlanArgs p) {
   const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t < p.n_out) p.rowmap[t] = plan_row(p, min(t, p.nk - 1));
+  if (t < p.n_out) {
+    const uint32_t row = plan_row(p, min(t, p.nk - 1));
+    p.rowmap[t] = row;
+    // The newest frame: its patch page is the last patch page of the table
+    // and its specials are the last visible tokens (it is always held).
+    const int d_patch = t - p.new_patch_begin;
+    const int d_spec = t - (p.nk - p.num_special);
+    uint32_t nrow = row;
+    if (d_patch >= 0 && d_patch < p.patch_len)
+      nrow = kOwnRow | uint32_t(p.num_special + d_patch);
+    else if (d_spec >= 0 && t < p.nk)
+      nrow = kOwnRow | uint32_t(d_spec);
+    p.rowmap_new[t] = nrow;
+  }
   if (t < p.n_out_own)
     p.rowmap_own[t] = t < p.nk ? plan_row(p, t) : kOwnRow | uint32_t(min(t - p.nk, p.n_own - 1));
 }
@@ -465,6 +478,51 @@ struct Runs {
   AttnArgs a[NB];
 };
 
+// This workgroup's share of a frame copy (see FrameCopy): the chunks
+// [part * n / parts, (part + 1) * n / parts), four 16-byte chunks per thread
+// in flight, every load of a round issued before its stores.  Nothing in the
+// launch reads the destination rows: its row map sends the newest frame's
+// tokens to the caller's buffers.
+__device__ __forceinline__ void copy_share(const FrameCopy& c, int part, int parts) {
+  const int64_t n = 2 * (int64_t(c.n_patch) + c.n_spec);
+  const int64_t lo = n * part / parts, hi = n * (part + 1) / parts;
+  const uint4* k = reinterpret_cast<const uint4*>(c.k);
+  const uint4* v = reinterpret_cast<const uint4*>(c.v);
+  uint4* pool = reinterpret_cast<uint4*>(c.pool);
+  constexpr int kU = 4;
+  for (int64_t base = lo + threadIdx.x; base < hi; base += int64_t(kU) * kThreads) {
+    uint4 buf[kU];
+    uint4* dst[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      int64_t i = base + int64_t(u) * kThreads;
+      i = i < hi ? i : hi - 1;   // past the share: re-read its last chunk, store nothing
+      const uint4* src;
+      if (i < c.n_patch) {
+        src = k + c.n_spec + i;
+        dst[u] = pool + c.pk + i;
+      } else if (i < 2 * int64_t(c.n_patch)) {
+        src = v + c.n_spec + (i - c.n_patch);
+        dst[u] = pool + c.pv + (i - c.n_patch);
+      } else if (i < 2 * int64_t(c.n_patch) + c.n_spec) {
+        src = k + (i - 2 * int64_t(c.n_patch));
+        dst[u] = pool + c.sk + (i - 2 * int64_t(c.n_patch));
+      } else {
+        const int64_t j = i - 2 * int64_t(c.n_patch) - c.n_spec;
+        src = v + j;
+        dst[u] = pool + c.sv + j;
+      }
+      buf[u] = *src;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      asm volatile("" : "+v"(buf[u].x), "+v"(buf[u].y), "+v"(buf[u].z), "+v"(buf[u].w));
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (base + int64_t(u) * kThreads < hi) *dst[u] = buf[u];
+  }
+}
+
 template <bool OWN, int NB>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const Runs<NB> runs) {
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageB];
@@ -487,6 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const Runs<NB> runs) 
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(a.nk, t_begin + a.tokens_per_split);
   if (t_begin >= t_end) return;  // the launch never makes an empty split
+  if (NB == 1 && a.copy.n_patch > 0) copy_share(a.copy, item, runs.n_items);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -22,6 +22,18 @@ struct AppendArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
+// The same copy done by the workgroups of an attention launch (a keyframe's
+// append folded into the block's run): four contiguous runs of 16-byte
+// chunks, [0, n_patch) K patch, [n_patch, 2 n_patch) V patch, then n_spec K
+// and n_spec V special chunks.  n_patch == 0: no copy.
+struct FrameCopy {
+  const uint16_t* k;      // caller's frame [tokens_per_frame][H][D]
+  const uint16_t* v;
+  uint16_t* pool;         // block's pool base
+  int64_t pk, pv, sk, sv; // destination offsets in 16-byte chunks
+  int32_t n_patch, n_spec;
+};
+
 // Expansion of a plan's page table into a per-token row map: for visible
 // token t, the pool row (page * 2 * page_size + offset) of its K; its V is
 // page_size rows further.  Entries past the last token repeat the last
@@ -54,6 +66,12 @@ struct PlanArgs {
   int32_t page_size;
   int32_t nk;               // visible tokens
   int32_t n_out;            // entries written (nk rounded up, plus padding)
+  // The third map serves a run that also copies the newest frame into the
+  // pool (append_frame_in_run): like the first, but the newest frame's
+  // tokens -- patch tokens from new_patch_begin, and the last num_special
+  // visible tokens -- are kOwnRow | their row in the caller's frame.
+  uint32_t* rowmap_new;     // out: n_out entries
+  int32_t new_patch_begin;  // first token of the newest frame's patch page
 };
 
 // Tiles the kernel uses; run() sizes the split from them.  One workgroup
@@ -82,6 +100,7 @@ struct AttnArgs {
   int32_t n_cached;         // tokens before the caller's own rows (nk without them)
   int32_t splits, tokens_per_split;
   float sm_scale;
+  FrameCopy copy;           // a keyframe's append done by this launch
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);

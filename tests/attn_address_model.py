@@ -63,10 +63,13 @@ def plan_rows(table, n_patch, specials, cfg):
     return np.concatenate(rows)
 
 
-def expand(rows, n_own):
-    """The two row maps the expansion kernel writes: run()'s (entries past the
-    last token repeat it) and run_own()'s (the caller's n_own rows after the
-    plan's tokens, marked; entries past them repeat the last)."""
+def expand(rows, n_own, new_patch_begin=None, num_special=6):
+    """The row maps the expansion kernel writes: run()'s (entries past the
+    last token repeat it), run_own()'s (the caller's n_own rows after the
+    plan's tokens, marked; entries past them repeat the last) and, given the
+    first token of the newest frame's patch page, the map of a run that
+    copies that frame (its patch tokens and the last num_special tokens
+    marked as rows of the caller's frame)."""
     nk = len(rows)
     n_out = round_up(nk, KEY_TILE) + ROW_PAD
     rm = rows[np.minimum(np.arange(n_out), nk - 1)]
@@ -74,7 +77,15 @@ def expand(rows, n_own):
     t = np.arange(n_out_own)
     rm_own = np.where(t < nk, rows[np.minimum(t, nk - 1)],
                       OWN | np.minimum(t - nk, n_own - 1))
-    return rm.astype(np.int64), rm_own.astype(np.int64)
+    if new_patch_begin is None:
+        return rm.astype(np.int64), rm_own.astype(np.int64)
+    t = np.arange(n_out)
+    patch_len = n_own - num_special
+    d_patch = t - new_patch_begin
+    d_spec = t - (nk - num_special)
+    rm_new = np.where((d_patch >= 0) & (d_patch < patch_len), OWN | (num_special + d_patch),
+                      np.where((d_spec >= 0) & (t < nk), OWN | d_spec, rm))
+    return rm.astype(np.int64), rm_own.astype(np.int64), rm_new.astype(np.int64)
 
 
 def item_of_block(n_items):

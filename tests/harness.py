@@ -31,10 +31,11 @@ def frame_kinds(wl, frames=None):
     return out
 
 
-def gpu_step(cache, wl, kind, reset, qkv, outs, stream=None, flags=(1, 0)):
+def gpu_step(cache, wl, kind, reset, qkv, outs, stream=None, flags=(1, 0), in_run=False):
     """One frame on the HIP side.  qkv[b] = (q, k, v) device tensors; the
     run's output for block b is written into outs[b]; evict_frames gets the
-    eviction flags (cross_frame_special, camera_only)."""
+    eviction flags (cross_frame_special, camera_only).  in_run: frames are
+    admitted with append_frame_in_run, so each block's run copies them."""
     S, W = wl.scale_frames, wl.sliding_window
     if reset:
         cache.reset()
@@ -44,7 +45,10 @@ def gpu_step(cache, wl, kind, reset, qkv, outs, stream=None, flags=(1, 0)):
         cache.set_defer_eviction(True)
     for b in range(wl.num_blocks):
         q, k, v = qkv[b]
-        cache.append_frame(b, k, v, stream=stream)
+        if in_run:
+            cache.append_frame_in_run(b, k, v, stream=stream)
+        else:
+            cache.append_frame(b, k, v, stream=stream)
         cache.evict_frames(b, S, W, *flags)
         if b == 0:
             cache.plan(stream=stream)

@@ -10,7 +10,9 @@ split is empty; the staged row-map reads stay inside the padded map; the
 mark in run_own's map; each tile's loads fill every LDS slot of its stage
 exactly once under the chunk swizzle; every pool load lies in the pool and
 every load of the caller's rows in the caller's frame; fragment reads stay
-inside a tile; queries, outputs, partials and the merge stay in range."""
+inside a tile; queries, outputs, partials and the merge stay in range.  The
+same for the map of a run that copies the newest frame, whose tokens it reads
+from the caller's frame."""
 
 import pytest
 
@@ -71,12 +73,16 @@ def test_attention_loads_stay_in_bounds(name, wl, frames, at, flags):
         table, n_patch, _ = c.get_plan()
         rows = M.plan_rows(table, n_patch, c.get_plan_specials(), cfg)
         nk = len(rows)
-        rm, rm_own = M.expand(rows, n_own)
+        first_new = (n_patch - 1) * wl.patch_tokens
+        rm, rm_own, rm_new = M.expand(rows, n_own, first_new, wl.num_special_tokens)
         for nq in sorted({1, wl.tokens_per_frame, 8 * wl.tokens_per_frame}):
             for s in SPLITS:
                 M.check_launch(rm, nk, nk, nq, wl.num_heads, wl.page_size, pool_bytes, s)
-                if pool_bytes <= 1 << 31:     # run_own takes pools up to 2 GiB
+                if pool_bytes <= 1 << 31:     # own rows need pools up to 2 GiB
                     M.check_launch(rm_own, nk + n_own, nk, nq, wl.num_heads, wl.page_size,
+                                   pool_bytes, s, own_frame_rows=n_own)
+                    # a run that copies the newest frame (append_frame_in_run)
+                    M.check_launch(rm_new, nk, first_new, nq, wl.num_heads, wl.page_size,
                                    pool_bytes, s, own_frame_rows=n_own)
         checked += 1
     c.close()

@@ -36,7 +36,7 @@ def log(msg):
 
 
 # ------------------------------------------------------------ small streams
-def full_parity(wl, frames=None, splits=0, flags=(1, 0)):
+def full_parity(wl, frames=None, splits=0, flags=(1, 0), in_run=False):
     """Every frame: whole-pool bytes, plan (with its visible special runs),
     stats, state bit-exact; attention on every row of every block.  Every
     evict_frames call passes the eviction flags."""
@@ -78,7 +78,7 @@ def full_parity(wl, frames=None, splits=0, flags=(1, 0)):
         if kind == "transient":
             o.set_defer_eviction(False)
 
-        H.gpu_step(cache, wl, kind, reset, qkv, outs, flags=flags)
+        H.gpu_step(cache, wl, kind, reset, qkv, outs, flags=flags, in_run=in_run)
         torch.cuda.synchronize()
         assert cache.get_plan() == plan_ref, f
         assert cache.get_plan_specials() == specials_ref, f
@@ -122,6 +122,95 @@ def test_tiny_stream_eviction_flags(flags):
     full_parity(tiny, flags=flags)
     full_parity(tiny.with_(keyframe_interval=2, frames=14, reset_every=9), flags=flags)
     full_parity(tiny.with_(dynamic=True, frames=20, seed=12), flags=flags)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_append_folded_into_run_small_streams(splits):
+    """append_frame_in_run + run: whole-pool bytes, plans and attention every
+    frame on the tiny stream (keyframes; interval 2 with a reset; dynamic
+    accept/rollback) and the 203-token-page stream with forced splits."""
+    tiny = synth.WORKLOADS["tiny"]
+    log(f"append in run, splits {splits}")
+    full_parity(tiny, splits=splits, in_run=True)
+    full_parity(tiny.with_(keyframe_interval=2, frames=14, reset_every=9), splits=splits,
+                in_run=True)
+    full_parity(tiny.with_(dynamic=True, frames=20, seed=13), splits=splits, in_run=True)
+    full_parity(MID.with_(frames=30), splits=splits, in_run=True)
+
+
+def test_append_folded_into_run_flushed_by_other_calls():
+    """A frame admitted by append_frame_in_run is copied before any call that
+    needs its bytes: the block's next append (both kinds), its rollback,
+    run_own, run_noalloc, run_batch and reset.  The pool bytes follow the
+    oracle, which copies at admission, after each of them."""
+    need_gpu()
+    import streaming_paged_kv_amd as spkv
+    wl = MID.with_(num_blocks=2, frames=12, keyframe_interval=1)
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    o = PagePoolOracle(cfg, track_pool=[0, 1])
+    cache = new_cache(wl)
+    S, W = wl.scale_frames, wl.sliding_window
+    sm = wl.head_dim ** -0.5
+
+    def admit(f, b, how):
+        q, k, v = synth.frame_qkv(wl, f, b, device=DEV)
+        if how == "in_run":
+            cache.append_frame_in_run(b, k, v)
+        else:
+            cache.append_frame(b, k, v)
+        o.append_frame(b, synth.bf16_bits(k), synth.bf16_bits(v))
+        return q, k, v
+
+    def same_pools(what):
+        torch.cuda.synchronize()
+        for b in range(2):
+            assert np.array_equal(synth.bf16_bits(cache.pools[b]), o.pools[b]), (what, b)
+
+    f = 0
+    # the block's next append, of either kind, copies the pending frame first
+    admit(f, 0, "in_run"); f += 1
+    admit(f, 0, "in_run"); f += 1      # copies frame 0; frame 1 waits
+    admit(f, 0, "plain"); f += 1       # copies frame 1
+    cache.evict_frames(0, S, W); o.evict_frames(0, S, W)
+    same_pools("next append")
+    # block 1 catches up so that both blocks hold the same frames
+    for g in range(f):
+        admit(g, 1, "plain")
+        cache.evict_frames(1, S, W); o.evict_frames(1, S, W)
+    # rollback under deferral
+    cache.set_defer_eviction(True); o.set_defer_eviction(True)
+    admit(f, 0, "in_run")
+    cache.rollback_last_frame(0); o.rollback_last_frame(0)
+    cache.set_defer_eviction(False); o.set_defer_eviction(False)
+    same_pools("rollback")
+    f += 1
+    # run_own / run_noalloc / run_batch on a block with a pending copy
+    for call in ("run_own", "run_noalloc", "run_batch"):
+        q, k, v = admit(f, 0, "in_run")
+        admit(f, 1, "plain")
+        for b in range(2):
+            cache.evict_frames(b, S, W); o.evict_frames(b, S, W)
+        cache.plan(); pl = o.plan()
+        if call == "run_own":
+            q2, k2, v2 = synth.frame_qkv(wl, f + 100, 0, device=DEV)
+            out = cache.run_own(0, q2, k2, v2)
+            from oracle.attention import paged_attention_with_own
+            ref = paged_attention_with_own(o.pools[0], pl, cfg, synth.bf16_bits(q2),
+                                           synth.bf16_bits(k2), synth.bf16_bits(v2), sm)
+        elif call == "run_noalloc":
+            out = cache.run_noalloc(0, q)
+            ref = paged_attention(o.pools[0], pl, cfg, synth.bf16_bits(q), sm)
+        else:
+            out = spkv.run_batch([dict(cache=cache, block=0, q=q)])[0]
+            ref = paged_attention(o.pools[0], pl, cfg, synth.bf16_bits(q), sm)
+        same_pools(call)
+        H.compare(out, ref, (call, f))
+        f += 1
+    # reset with a pending copy
+    admit(f, 0, "in_run")
+    cache.reset(); o.reset()
+    same_pools("reset")
+    cache.close()
 
 
 @pytest.mark.parametrize("flags,splits", [((1, 1), 0), ((0, 0), 3), ((0, 1), 7)])
@@ -500,7 +589,7 @@ def test_constant_v_is_reproduced():
 
 # ------------------------------------------------------- full-size streams
 def full_size(name, num_blocks=None, attn_blocks=(0, 11, 23), pool_blocks=(0, 23),
-              frames=None, milestone_keys=None, flags=(1, 0)):
+              frames=None, milestone_keys=None, flags=(1, 0), in_run=False):
     """The workload's whole stream on the GPU, with the oracle checking every
     plan and state bit-exact, and at milestone frames the attention of
     sampled rows (all heads) and the bytes of the visible pages."""
@@ -575,7 +664,7 @@ def full_size(name, num_blocks=None, attn_blocks=(0, 11, 23), pool_blocks=(0, 23
 
         specials_ref = special_runs(o.plan_state.spec_vis)
         # HIP side
-        H.gpu_step(cache, wl, kind, reset, qkv, outs, flags=flags)
+        H.gpu_step(cache, wl, kind, reset, qkv, outs, flags=flags, in_run=in_run)
         assert cache.get_plan() == plan_ref, f
         assert cache.get_plan_specials() == specials_ref, f
         if f in milestones:
@@ -611,6 +700,15 @@ def test_full_518x378_padded_long_stream():
 
 def test_full_dynamic_stream():
     full_size("dynamic")
+
+
+def test_full_518x378_stream_appends_folded_into_runs():
+    """The 518x378 stream with every frame admitted by append_frame_in_run:
+    each block's run copies the frame into its pages and reads its tokens
+    from the caller's buffers (transient frames too, before their rollback);
+    plans every frame, attention and the visible pages' bytes at milestones;
+    four blocks."""
+    full_size("518x378", num_blocks=4, attn_blocks=(0, 3), pool_blocks=(0, 3), in_run=True)
 
 
 def test_full_518x378_stream_camera_tokens_only():
