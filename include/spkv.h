@@ -235,7 +235,10 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream);
  * live and special state differ from block 0's at plan time.  UNSUPPORTED
  * when a block's pool exceeds 4 GiB (pool rows are addressed by 32-bit byte
  * offsets).  Enqueues the attention kernel (and, when the key range is split,
- * a merge kernel) and nothing else, so a run of a planned frame may be
+ * a merge kernel) and nothing else -- except that a frame admitted to this
+ * block by spkv_append_frame_in_run is copied into its pages by that same
+ * attention launch (or, when the launch cannot fold it, by a plain copy
+ * enqueued first) -- so a run of a planned frame may be
  * captured into a HIP graph; plan() may not, since it copies the host
  * allocator's state of the moment.  A captured run binds the device row map
  * of the plan that was current at capture (plans alternate between two
