@@ -887,13 +887,16 @@ def test_batch_mode_518x378_scale_frames():
 
 
 # ------------------------------------------------------ random schedules
-@pytest.mark.parametrize("seed", [101, 102, 103])
-def test_random_schedules_every_frame(seed):
+@pytest.mark.parametrize("seed,variants", [(101, False), (102, False), (103, False),
+                                           (301, True), (302, True), (303, True)])
+def test_random_schedules_every_frame(seed, variants):
     """Seeded random mixes of keyframes, transient (append + rollback)
     non-keyframes, run_own non-keyframes, deferred accept / reject and resets
     on a 2-block stream with 16-token pages: after every frame the whole pool,
-    the plan, the stats and the allocator state are bit-exact, and every
-    attention output matches the oracle."""
+    the plan (with its visible special runs), the stats and the allocator
+    state are bit-exact, and every attention output matches the oracle.  With
+    variants, each frame also draws its eviction flags and whether its
+    appends are folded into the runs (append_frame_in_run)."""
     need_gpu()
     from oracle.attention import paged_attention_with_own
     rng = np.random.default_rng(seed)
@@ -908,6 +911,11 @@ def test_random_schedules_every_frame(seed):
     committed = 0
     for f in range(wl.frames):
         ev = rng.choice(["key", "key", "transient", "own", "accept", "reject", "reset"])
+        flags = (1, 0)
+        in_run = False
+        if variants:
+            flags = [(1, 0), (1, 1), (0, 0), (0, 1)][int(rng.integers(0, 4))]
+            in_run = bool(rng.integers(0, 2))
         if ev == "reset" or committed >= 30:       # 32 special slots: stay clear of overflow
             cache.reset()
             o.reset()
@@ -933,13 +941,17 @@ def test_random_schedules_every_frame(seed):
                 cache.set_defer_eviction(True)
                 o.set_defer_eviction(True)
             for b in range(nb):
-                cache.append_frame(b, qkv[b][1], qkv[b][2])
+                if in_run:
+                    cache.append_frame_in_run(b, qkv[b][1], qkv[b][2])
+                else:
+                    cache.append_frame(b, qkv[b][1], qkv[b][2])
                 o.append_frame(b, bits[b][1], bits[b][2])
-                cache.evict_frames(b, S, W)
-                o.evict_frames(b, S, W)
+                cache.evict_frames(b, S, W, *flags)
+                o.evict_frames(b, S, W, *flags)
                 if b == 0:
                     cache.plan()
                     o.plan()
+                    assert cache.get_plan_specials() == special_runs(o.plan_state.spec_vis)
                 out = cache.run(b, qkv[b][0])
                 ref = paged_attention(o.pools[b], o.check_run(b), cfg, bits[b][0], sm)
                 torch.cuda.synchronize()
@@ -959,6 +971,7 @@ def test_random_schedules_every_frame(seed):
         for b in range(nb):
             assert list(o.block_state(b)) == list(cache.get_block_state(b)), (seed, f, b)
             assert tuple(o.get_cache_stats(b)) == cache.get_cache_stats(b), (seed, f, b)
+            assert o.special_visibility(b) == cache.get_block_specials(b), (seed, f, b)
             assert np.array_equal(synth.bf16_bits(cache.pools[b]), o.pools[b]), (seed, f, b)
     cache.close()
 
