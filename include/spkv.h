@@ -245,7 +245,9 @@ SPKV_API int spkv_plan(spkv_handle* h, void* hip_stream);
  * slots), its visible-token count and its split: a replay is valid only
  * while that plan is still the current one, i.e. until the next plan() or
  * reset().  Replayed after that, it attends over whatever the slot then
- * holds. */
+ * holds.  A captured run that folds a frame's copy (append_frame_in_run)
+ * copies it at every replay, not at capture; the same bytes land in the same
+ * pages each time, which stays harmless while the plan is current. */
 SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
                       int32_t nq, float sm_scale, void* hip_stream);
 

@@ -130,6 +130,33 @@ def test_tiny_stream_worked_example_through_abi(golden_dir):
     c.close()
 
 
+def test_append_in_run_admits_like_append():
+    """On a host-only handle append_frame_in_run is append_frame: the same
+    state, plans and errors over a stream with evictions, deferral, rollback
+    and the special stream filling up."""
+    cfg = CFGS[0]
+    a = spkv.PagedKVCache(host_only=True, **cfg)
+    b = spkv.PagedKVCache(host_only=True, **cfg)
+    S, W = cfg["scale_frames"], cfg["sliding_window"]
+    for f in range(40):
+        defer = f % 5 == 3
+        for c in (a, b):
+            c.set_defer_eviction(defer)
+        r = (code_of(a.append_frame, 0), code_of(b.append_frame_in_run, 0))
+        assert r[0] == r[1], (f, r)
+        a.evict_frames(0, S, W, 1, f % 3 == 0)
+        b.evict_frames(0, S, W, 1, f % 3 == 0)
+        if defer:
+            assert code_of(a.rollback_last_frame, 0) == code_of(b.rollback_last_frame, 0)
+        assert a.get_block_state(0) == b.get_block_state(0)
+        assert a.get_block_specials(0) == b.get_block_specials(0)
+        if a.get_cache_stats(0)[0]:
+            a.plan(); b.plan()
+            assert a.get_plan() == b.get_plan()
+    assert code_of(b.append_frame_in_run, 5) == "BAD_BLOCK"
+    a.close(); b.close()
+
+
 def test_eviction_flags_worked_example_through_abi(golden_dir):
     """The hand-derived eviction-flag example, replayed on the C++ allocator."""
     import json, os
