@@ -115,10 +115,11 @@ SPKV_API int spkv_query_sizes(const spkv_config* cfg, int64_t* max_num_pages,
 
 /* Workspace that lets run() split the key range of nq query rows across
  * num_splits workgroups: min_workspace_bytes plus num_splits partial
- * results of nq * H * (D + 2) * 4 bytes (fp32 O, running maximum and sum).
+ * results of nq * H * (2 * D + 8) bytes (each split's output normalised by
+ * its row sum in bf16, and its fp32 running maximum and sum).
  * run() uses up to 32 splits, and fewer when the workspace holds fewer.
  * [LB-PERF] "Persistent Workspace Pre-allocation" pre-allocates 128 MiB; at
- * 1005 query rows x 16 heads that holds 31 splits.  This call is an addition
+ * 1005 query rows x 16 heads that holds more than the 32 splits run() uses.  This call is an addition
  * of this library (the pages size no workspace by formula).  1 <= nq <=
  * 2^20, 1 <= num_splits <= 32, else INVALID_ARG. */
 SPKV_API int spkv_query_workspace(const spkv_config* cfg, int32_t nq, int32_t num_splits,
@@ -258,8 +259,8 @@ SPKV_API int spkv_run(spkv_handle* h, int32_t block, const void* q, void* out,
  * array per GPU (allocated when the library's code is loaded on that GPU and
  * held until the process ends), instead of in the handle's workspace.  So a
  * handle created with only min_workspace_bytes still gets run()'s split.
- * The call allocates nothing.  Limit: nq <= 48 MiB / (2 * H * (D + 2) * 4)
- * rounded down (two splits of partials; 5957 rows at H = 16), else
+ * The call allocates nothing.  Limit: nq <= 48 MiB / (2 * H * (2 * D + 8))
+ * rounded down (two splits of partials; 11565 rows at H = 16), else
  * SPKV_ERR_WORKSPACE and nothing is enqueued.  Every call on one GPU shares
  * that GPU's array, whatever the handle: two calls whose kernels overlap in
  * time on one GPU (different streams, no ordering between them) race on it

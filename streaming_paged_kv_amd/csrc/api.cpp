@@ -56,11 +56,11 @@ struct Sizes {
       rowmap_bytes, rowmap_own_bytes, min_ws;
 };
 
-// Split partials of nq query rows: fp32 O and (m, l) per (query, head) row
-// and split.
+// Split partials of nq query rows: each split's O normalised by its row sum
+// (bf16) and its fp32 (m, l) per (query, head) row and split.
 int64_t partial_bytes(const spkv::Geometry& g, int64_t nq, int64_t splits) {
   const int64_t rows = nq * g.num_heads;
-  return round_up(rows * g.head_dim * 4 * splits, kAlign) + round_up(rows * 8 * splits, kAlign);
+  return round_up(rows * g.head_dim * 2 * splits, kAlign) + round_up(rows * 8 * splits, kAlign);
 }
 
 Sizes sizes_of(const spkv::Geometry& g) {
@@ -576,9 +576,9 @@ spkv::AttnArgs make_run(spkv_handle* h, int32_t block, const void* q, void* out,
   a.rowmap = own ? h->dev_rowmap_own[h->plan_slot] : h->dev_rowmap[h->plan_slot];
   a.q = static_cast<const uint16_t*>(q);
   a.out = static_cast<uint16_t*>(out);
-  a.part_o = reinterpret_cast<float*>(part.base);
+  a.part_o = reinterpret_cast<uint16_t*>(part.base);
   a.part_ml = reinterpret_cast<float*>(
-      part.base + round_up(rows * g.head_dim * 4 * splits, kAlign));
+      part.base + round_up(rows * g.head_dim * 2 * splits, kAlign));
   a.nq = nq;
   a.num_heads = g.num_heads;
   a.page_size = g.page_size;
@@ -593,7 +593,7 @@ spkv::AttnArgs make_run(spkv_handle* h, int32_t block, const void* q, void* out,
 // Query rows run_noalloc() takes: the library's scratch must hold two
 // splits of their partials.
 int64_t noalloc_max_rows(const spkv::Geometry& g) {
-  int64_t n = spkv::kScratchBytes / (2 * int64_t(g.num_heads) * (g.head_dim + 2) * 4);
+  int64_t n = spkv::kScratchBytes / (2 * int64_t(g.num_heads) * (g.head_dim * 2 + 8));
   while (n > 0 && partial_bytes(g, n, 2) > spkv::kScratchBytes) --n;
   return n;
 }

@@ -656,16 +656,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const Runs<NB> runs) 
           *reinterpret_cast<uint2*>(dst + d0) = wv;
         }
     } else {
+      // This split's O normalised by its own row sum, in bf16, beside its
+      // (m, l) in fp32: the merge weighs each split by 2^(m_s - M) l_s.
       const size_t row = (size_t(split) * a.nq + qi) * a.num_heads + h;
-      float* dst = a.part_o + row * kD;
+      const float inv = 1.0f / l_tot;
+      uint16_t* dst = a.part_o + row * kD;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int d0 = 32 * dt + rr * 8 + half * 4;
-          *reinterpret_cast<float4*>(dst + d0) =
-              make_float4(o_acc[nt][dt][4 * rr + 0], o_acc[nt][dt][4 * rr + 1],
-                          o_acc[nt][dt][4 * rr + 2], o_acc[nt][dt][4 * rr + 3]);
+          const __bf16 b0 = (__bf16)(o_acc[nt][dt][4 * rr + 0] * inv);
+          const __bf16 b1 = (__bf16)(o_acc[nt][dt][4 * rr + 1] * inv);
+          const __bf16 b2 = (__bf16)(o_acc[nt][dt][4 * rr + 2] * inv);
+          const __bf16 b3 = (__bf16)(o_acc[nt][dt][4 * rr + 3] * inv);
+          uint2 wv;
+          wv.x = uint32_t(__builtin_bit_cast(uint16_t, b0)) |
+                 (uint32_t(__builtin_bit_cast(uint16_t, b1)) << 16);
+          wv.y = uint32_t(__builtin_bit_cast(uint16_t, b2)) |
+                 (uint32_t(__builtin_bit_cast(uint16_t, b3)) << 16);
+          *reinterpret_cast<uint2*>(dst + d0) = wv;
         }
       if (half == 0)
         *reinterpret_cast<float2*>(a.part_ml + row * 2) = make_float2(m_run[nt], l_tot);
@@ -673,14 +683,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const Runs<NB> runs) 
   }
 }
 
-// Combine the splits of each (query, head): with m the reference (base 2)
-// and l the sum of each split, O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Combine the splits of each (query, head): with m the reference (base 2),
+// l the sum and O_s / l_s the normalised output of each split,
+// O = sum_s 2^(m_s - M) l_s (O_s / l_s) / sum_s 2^(m_s - M) l_s.
 // One thread per (query, head, 4 dims).  Splits are read eight at a time with
 // all their loads in flight together (this kernel is latency-bound); splits
 // past the count re-read the last one and get weight 0.
 constexpr int kMergeGroup = 8;
 
-__device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ void merge_row(const uint16_t* __restrict__ part_o,
                                          const float* __restrict__ part_ml,
                                          uint16_t* __restrict__ out, int rows, int splits,
                                          int gid) {
@@ -695,12 +709,12 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
   float lsum = 0.f;
   for (int s0 = 0; s0 < splits; s0 += kMergeGroup) {
     float2 ml[kMergeGroup];
-    float4 ov[kMergeGroup];
+    uint2 ov[kMergeGroup];
 #pragma unroll
     for (int j = 0; j < kMergeGroup; ++j) {
       const size_t r = size_t(min(s0 + j, splits - 1)) * rows + row;
       ml[j] = *reinterpret_cast<const float2*>(part_ml + r * 2);
-      ov[j] = *reinterpret_cast<const float4*>(part_o + r * kD + d0);
+      ov[j] = *reinterpret_cast<const uint2*>(part_o + r * kD + d0);
     }
     float gmax = mmax;
 #pragma unroll
@@ -716,12 +730,13 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
     mmax = gmax;
 #pragma unroll
     for (int j = 0; j < kMergeGroup; ++j) {
-      const float w = s0 + j < splits ? __builtin_amdgcn_exp2f(ml[j].x - mmax) : 0.f;
-      acc.x += w * ov[j].x;
-      acc.y += w * ov[j].y;
-      acc.z += w * ov[j].z;
-      acc.w += w * ov[j].w;
-      lsum += w * ml[j].y;
+      const float w =
+          s0 + j < splits ? __builtin_amdgcn_exp2f(ml[j].x - mmax) * ml[j].y : 0.f;
+      acc.x += w * bf16_lo(ov[j].x);
+      acc.y += w * bf16_hi(ov[j].x);
+      acc.z += w * bf16_lo(ov[j].y);
+      acc.w += w * bf16_hi(ov[j].y);
+      lsum += w;
     }
   }
   const float inv = 1.0f / lsum;
@@ -735,7 +750,7 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
   *reinterpret_cast<uint2*>(out + size_t(row) * kD + d0) = w;
 }
 
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(256) void merge_kernel(const uint16_t* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     uint16_t* __restrict__ out,
                                                     int rows, int splits) {
@@ -748,7 +763,7 @@ template <int NB>
 struct Merges {
   int32_t end_block[NB];
   int32_t rows[NB], splits[NB];
-  const float* part_o[NB];
+  const uint16_t* part_o[NB];
   const float* part_ml[NB];
   uint16_t* out[NB];
 };

@@ -93,8 +93,8 @@ struct AttnArgs {
   const uint32_t* rowmap;   // token -> K row of the pool (see PlanArgs)
   const uint16_t* q;        // [nq][H][D]
   uint16_t* out;            // [nq][H][D]
-  float* part_o;            // [splits][nq][H][D]     (splits > 1)
-  float* part_ml;           // [splits][nq][H][2]     (splits > 1)
+  uint16_t* part_o;         // [splits][nq][H][D] bf16, each split's O / l (splits > 1)
+  float* part_ml;           // [splits][nq][H][2]     (m, l)         (splits > 1)
   int32_t nq, num_heads, page_size;
   int32_t nk;               // visible tokens
   int32_t n_cached;         // tokens before the caller's own rows (nk without them)

@@ -58,9 +58,10 @@ def test_query_sizes_518_exact_and_padded():
     # the pages' 128 MiB workspace holds at least 16 key splits here
     per_split = (wfull - wmin) // 32
     assert (128 * 2 ** 20 - wmin) // per_split >= 16
-    # one split of one frame: fp32 O and (m, l) for 1005 rows x 16 heads
+    # one split of one frame: bf16 normalised O and fp32 (m, l) for 1005
+    # rows x 16 heads
     w1 = spkv.query_workspace(1005, 1, page_size=999, **kw)
-    assert w1 - spkv.query_sizes(page_size=999, **kw)[2] == 1005 * 16 * 64 * 4 + 1005 * 16 * 8 + 128   # 256-byte rounding
+    assert w1 - spkv.query_sizes(page_size=999, **kw)[2] == 1005 * 16 * 64 * 2 + 1005 * 16 * 8 + 128   # 256-byte rounding
     for nq, sp in ((0, 1), (1, 0), (1, 33), ((1 << 20) + 1, 1)):
         with pytest.raises(spkv.SpkvError):
             spkv.query_workspace(nq, sp, page_size=999, **kw)
