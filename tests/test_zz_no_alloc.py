@@ -72,8 +72,10 @@ def test_run_noalloc_matches_run():
             assert torch.equal(a, b), (call, sp)
             H.compare(b, ref, ("noalloc forced", call, sp))
         full.set_num_splits(0)
-    # beyond the array's limit (two splits of 16-head rows): refused, nothing written
-    limit = (48 << 20) // (2 * 16 * 66 * 4)
+    # beyond the array's limit (two splits of 16-head rows, each row's
+    # partial a bf16 O of 64 dims and an fp32 (m, l)): refused, nothing written
+    limit = (48 << 20) // (2 * 16 * (64 * 2 + 8))
+    assert limit == 11565
     q = torch.zeros((limit + 1, 16, 64), dtype=torch.bfloat16, device=DEV)
     out = torch.full_like(q, 7.0)
     with pytest.raises(spkv.SpkvError) as ei:
