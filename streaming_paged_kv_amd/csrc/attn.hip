@@ -278,7 +278,9 @@ __device__ __forceinline__ void mfma_phase(const char* vtile, const char* ktile,
 // 8*(lane/32)+j of each 16-key step); returns the lane's partial row sum.
 __device__ __forceinline__ float exp_pack(const f32x16 (&x)[2], float c, float mneg,
                                           bf16x8 (&pf)[4]) {
-  float s0 = 0.f, s1 = 0.f;
+  // The two sums start at the first two p values (not at 0: 0 + p is not
+  // folded away, since the compiler cannot know that p is never -0).
+  float s0, s1;
 #pragma unroll
   for (int k2 = 0; k2 < 4; ++k2) {
     const int mt = k2 >> 1, r0 = (k2 & 1) * 8;
@@ -287,8 +289,8 @@ __device__ __forceinline__ float exp_pack(const f32x16 (&x)[2], float c, float m
     for (int jj = 0; jj < 8; jj += 2) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(x[mt][r0 + jj], c, mneg));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(x[mt][r0 + jj + 1], c, mneg));
-      s0 += p0;
-      s1 += p1;
+      s0 = k2 == 0 && jj == 0 ? p0 : s0 + p0;
+      s1 = k2 == 0 && jj == 0 ? p1 : s1 + p1;
       v[jj] = (__bf16)p0;
       v[jj + 1] = (__bf16)p1;
     }
