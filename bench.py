@@ -424,15 +424,6 @@ def main():
     #      the append kernel's bandwidth.
     ev_attn, ev_app = [], []
     flops, app_bytes = [], []
-    # Timing events are created up front (and their first record issued
-    # here), so that window B's host loop only records them.
-    ev_pool = [torch.cuda.Event(enable_timing=True)
-               for _ in range(2 * nb * n_attn + 2 * n_app)]
-    for e in ev_pool:
-        e.record(stream)
-
-    def new_event():
-        return ev_pool.pop()
 
     def planned_tokens():
         tab, npatch, lpl = cache.get_plan()
@@ -454,8 +445,8 @@ def main():
             for b in range(nb):
                 q, k, v = qkv[b]
                 if mode == "B":
-                    a0 = new_event()
-                    a1 = new_event()
+                    a0 = torch.cuda.Event(enable_timing=True)
+                    a1 = torch.cuda.Event(enable_timing=True)
                     a0.record(stream)
                 cache.run_own(b, q, k, v, out=outs[b], sm_scale=sm, stream=stream)
                 if mode == "B":
@@ -476,8 +467,8 @@ def main():
             # The frame's appends of all blocks back to back between two
             # events (blocks are independent, so appending every block before
             # the first evict/plan/run leaves each block's steps in order).
-            e0 = new_event()
-            e1 = new_event()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for b in range(nb):
                 cache.append_frame(b, qkv[b][1], qkv[b][2], stream=stream)
@@ -494,8 +485,8 @@ def main():
                 if mode == "B":
                     nk = planned_tokens()
             if mode == "B":
-                a0 = new_event()
-                a1 = new_event()
+                a0 = torch.cuda.Event(enable_timing=True)
+                a1 = torch.cuda.Event(enable_timing=True)
                 a0.record(stream)
             cache.run(b, q, out=outs[b], sm_scale=sm, stream=stream)
             if mode == "B":
