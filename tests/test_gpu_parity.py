@@ -1316,3 +1316,56 @@ def test_run_own_and_run_batch_captured_in_a_hip_graph():
         del g
     for c in caches:
         c.close()
+
+
+def test_run_folding_a_copy_captured_in_a_hip_graph():
+    """A run that folds the copy of a frame admitted by append_frame_in_run,
+    captured into a HIP graph: the copy belongs to the captured attention
+    launch, so it happens at every replay and not at capture.  After each
+    replay the whole pool equals the oracle's (which copies at admission)
+    and the output equals, bit for bit, the same run done eagerly on a twin
+    cache that admitted the frame with append_frame (same bytes, same order,
+    same split); eager work and synchronisation between replays."""
+    need_gpu()
+    wl = MID.with_(name="graph-fold", num_blocks=1, frames=9, keyframe_interval=1, seed=67)
+    cfg = OracleConfig(**wl.cfg_kwargs())
+    o = PagePoolOracle(cfg, track_pool=[0])
+    fold, twin = new_cache(wl), new_cache(wl)
+    S, W = wl.scale_frames, wl.sliding_window
+    sm = wl.head_dim ** -0.5
+    frames = [synth.frame_qkv(wl, f, 0, device=DEV) for f in range(wl.frames)]
+    for f, (q, k, v) in enumerate(frames):
+        fold.append_frame_in_run(0, k, v)
+        twin.append_frame(0, k, v)
+        o.append_frame(0, synth.bf16_bits(k), synth.bf16_bits(v))
+        for c in (fold, twin):
+            c.evict_frames(0, S, W)
+            c.plan()
+        o.evict_frames(0, S, W)
+        pl = o.plan()
+        if f < wl.frames - 1:
+            fold.run(0, q, sm_scale=sm)     # folds frame f's copy, eagerly
+            twin.run(0, q, sm_scale=sm)
+    q = frames[-1][0]
+    ref = twin.run(0, q, sm_scale=sm)
+    torch.cuda.synchronize()
+    H.compare(ref, paged_attention(o.pools[0], pl, cfg, synth.bf16_bits(q), sm), "twin")
+    out = torch.empty_like(q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fold.run(0, q, out=out, sm_scale=sm)
+    torch.cuda.synchronize()
+    # the frame's page (never written before) still differs: nothing copied yet
+    assert not np.array_equal(synth.bf16_bits(fold.pools[0]), o.pools[0])
+    for i in range(3):
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), i
+        assert np.array_equal(synth.bf16_bits(fold.pools[0]), o.pools[0]), i
+        junk = torch.randn(1 << 20, device=DEV)
+        assert torch.isfinite(junk.sum())
+        torch.cuda.synchronize()
+    del g
+    fold.close()
+    twin.close()
