@@ -1080,8 +1080,9 @@ def test_run_batch_rejects_overlapping_requests():
 
 @pytest.mark.parametrize("seed", [201, 202])
 def test_run_batch_random_schedules(seed):
-    """Three streams of different geometry, each with its own seeded random
-    mix of keyframes, transient non-keyframes, run_own non-keyframes,
+    """Three streams of different geometry and eviction flags (all specials,
+    camera tokens only, none of an evicted frame), each with its own seeded
+    random mix of keyframes, transient non-keyframes, run_own non-keyframes,
     deferred accept / reject and resets; per frame and block one run_batch
     covers the three streams.  After every frame each stream's whole pool,
     stats and allocator state are bit-exact and every output matches the
@@ -1094,6 +1095,7 @@ def test_run_batch_random_schedules(seed):
            synth.Workload("odd", 2, 2, 64, 13, 11, 4, 1, 3, 1, 40, 30, seed=seed + 1),
            MID.with_(name="mid2", frames=30, seed=seed + 2)]
     nb = 2
+    flags = [(1, 0), (1, 1), (0, 0)]
     cfgs = [OracleConfig(**w.cfg_kwargs()) for w in wls]
     oracles = [PagePoolOracle(cfg, track_pool=range(nb)) for cfg in cfgs]
     caches = [new_cache(w) for w in wls]
@@ -1136,8 +1138,8 @@ def test_run_batch_random_schedules(seed):
                 else:
                     c.append_frame(b, k, v)
                     o.append_frame(b, kb, vb)
-                    c.evict_frames(b, S, W)
-                    o.evict_frames(b, S, W)
+                    c.evict_frames(b, S, W, *flags[i])
+                    o.evict_frames(b, S, W, *flags[i])
                     if b == 0:
                         c.plan()
                         o.plan()
