@@ -4,7 +4,19 @@
  * of a few calls whose result the contract fixes.  tests/test_c_client.py
  * builds it with gcc, runs it and checks the output.
  *
- * usage: c_abi_client NB H D PS P NS S W R MTF FRAMES */
+ * usage: c_abi_client NB H D PS P NS S W R MTF FRAMES
+ *        c_abi_client script NB H D PS P NS S W R MTF < commands
+ *
+ * Script mode reads one command per line and applies it to block 0 of a
+ * host-only handle, printing "<command> <code>" for each:
+ *   a          append_frame_in_run        A      append_frame
+ *   e C M      evict_frames with cross_frame_special C and camera_only M
+ *   d E        set_defer_eviction(E)      x      execute_deferred_eviction
+ *   r          rollback_last_frame
+ *   p          plan, then the plan's table, last_page_len, special runs, the
+ *              block's special runs and its free list on the same line
+ *   c          the codes of run, run_own, run_noalloc (host-only: all checks,
+ *              then UNSUPPORTED) and set_num_splits(3) and (-1) */
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -18,6 +30,65 @@ static void print_list(const char* tag, const int32_t* v, int32_t n) {
   for (i = 0; i < n; ++i) printf(" %d", (int)v[i]);
 }
 
+static int script(spkv_config* c) {
+  static int32_t table[CAP], runs[3 * CAP], scale[CAP], live[CAP], free_list[CAP];
+  int32_t n_pages, n_patch, lpl, n_runs, n_scale, n_live, n_free;
+  int64_t nsf;
+  spkv_handle* h = NULL;
+  char cmd[8];
+  int a1, a2, rc;
+  const int32_t nq = c->num_special_tokens + c->patch_tokens;
+  rc = spkv_create(c, NULL, NULL, 0, &h);
+  printf("create %d\n", rc);
+  if (rc != SPKV_OK) return 1;
+  while (scanf("%7s", cmd) == 1) {
+    switch (cmd[0]) {
+      case 'a': printf("a %d\n", spkv_append_frame_in_run(h, 0, NULL, NULL, NULL)); break;
+      case 'A': printf("A %d\n", spkv_append_frame(h, 0, NULL, NULL, NULL)); break;
+      case 'e':
+        if (scanf("%d %d", &a1, &a2) != 2) return 1;
+        printf("e %d\n", spkv_evict_frames(h, 0, c->scale_frames, c->sliding_window, a1, a2));
+        break;
+      case 'd':
+        if (scanf("%d", &a1) != 1) return 1;
+        printf("d %d\n", spkv_set_defer_eviction(h, a1));
+        break;
+      case 'x':
+        printf("x %d\n", spkv_execute_deferred_eviction(h, 0, c->scale_frames,
+                                                          c->sliding_window));
+        break;
+      case 'r': printf("r %d\n", spkv_rollback_last_frame(h, 0)); break;
+      case 'p':
+        rc = spkv_plan(h, NULL);
+        printf("p %d", rc);
+        if (rc == SPKV_OK) {
+          if (spkv_get_plan(h, table, CAP, &n_pages, &n_patch, &lpl) != SPKV_OK) return 1;
+          print_list("table", table, n_pages);
+          printf(" lpl %d", (int)lpl);
+          if (spkv_get_plan_specials(h, runs, CAP, &n_runs) != SPKV_OK) return 1;
+          print_list("pspec", runs, 3 * n_runs);
+          if (spkv_get_block_specials(h, 0, runs, CAP, &n_runs) != SPKV_OK) return 1;
+          print_list("bspec", runs, 3 * n_runs);
+          if (spkv_get_block_state(h, 0, scale, live, free_list, CAP, &n_scale, &n_live,
+                                   &n_free, &nsf) != SPKV_OK)
+            return 1;
+          print_list("free", free_list, n_free);
+        }
+        printf("\n");
+        break;
+      case 'c':
+        printf("c %d %d %d %d %d\n", spkv_run(h, 0, NULL, NULL, nq, 0.125f, NULL),
+               spkv_run_own(h, 0, NULL, NULL, nq, 0.125f, NULL, NULL, NULL),
+               spkv_run_noalloc(h, 0, NULL, NULL, nq, 0.125f, NULL),
+               spkv_set_num_splits(h, 3), spkv_set_num_splits(h, -1));
+        break;
+      default: return 1;
+    }
+  }
+  printf("destroy %d\n", spkv_destroy(h));
+  return 0;
+}
+
 int main(int argc, char** argv) {
   spkv_config c;
   spkv_handle* h = NULL;
@@ -28,6 +99,19 @@ int main(int argc, char** argv) {
   spkv_stats st;
   spkv_request req[2];
   int frames, f, rc;
+  if (argc == 12 && argv[1][0] == 's') {
+    c.num_blocks = atoi(argv[2]);
+    c.num_heads = atoi(argv[3]);
+    c.head_dim = atoi(argv[4]);
+    c.page_size = atoi(argv[5]);
+    c.patch_tokens = atoi(argv[6]);
+    c.num_special_tokens = atoi(argv[7]);
+    c.scale_frames = atoi(argv[8]);
+    c.sliding_window = atoi(argv[9]);
+    c.headroom = atoi(argv[10]);
+    c.max_total_frames = atoi(argv[11]);
+    return script(&c);
+  }
   if (argc != 12) {
     fprintf(stderr, "usage: %s NB H D PS P NS S W R MTF FRAMES\n", argv[0]);
     return 2;
