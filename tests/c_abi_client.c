@@ -16,7 +16,8 @@
  *   p          plan, then the plan's table, last_page_len, special runs, the
  *              block's special runs and its free list on the same line
  *   c          the codes of run, run_own, run_noalloc (host-only: all checks,
- *              then UNSUPPORTED) and set_num_splits(3) and (-1) */
+ *              then UNSUPPORTED) and set_num_splits(3) and (-1)
+ *   R          reset                      s      get_cache_stats, printed */
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -58,6 +59,14 @@ static int script(spkv_config* c) {
                                                           c->sliding_window));
         break;
       case 'r': printf("r %d\n", spkv_rollback_last_frame(h, 0)); break;
+      case 'R': printf("R %d\n", spkv_reset(h)); break;
+      case 's': {
+        spkv_stats st;
+        rc = spkv_get_cache_stats(h, 0, &st);
+        printf("s %d %lld %d %d %d %lld\n", rc, (long long)st.frame_count, (int)st.scale_pages,
+               (int)st.live_pages, (int)st.free_pages, (long long)st.special_tokens);
+        break;
+      }
       case 'p':
         rc = spkv_plan(h, NULL);
         printf("p %d", rc);
