@@ -162,7 +162,8 @@ SPKV_API int spkv_append_frame(spkv_handle* h, int32_t block, const void* k,
  * a run that cannot fold the copy (a pool over 2 GiB, or a plan that is not
  * the one of this frame), reset or destroy -- the library enqueues the plain
  * copy on hip_stream first.  k and v must therefore stay valid and unchanged
- * until that copy has run (the pool's bytes end up the same either way). */
+ * until that copy has run, and hip_stream until it has been enqueued (the
+ * pool's bytes end up the same either way). */
 SPKV_API int spkv_append_frame_in_run(spkv_handle* h, int32_t block, const void* k,
                                       const void* v, void* hip_stream);
 
